@@ -1,0 +1,95 @@
+// combine.hip -- the layer-boundary SUM of rowwise partials on one device.
+//
+// Diffusers "Tensor parallelism" page: rowwise ranks each produce a partial
+// sum and one AllReduce at the block boundary rebuilds the output (opening
+// definition; "Colwise and rowwise", pairing rule).  With every rank's partial
+// buffer on one device the reduction is this kernel:
+//   out = ((p_0 + p_1) + ... + p_{P-1}) + bias
+// in fp32, in ascending part order (a fixed order makes the result unique and
+// reproducible), the bias added once, one rounding to the output dtype.
+// HBM-bound: each thread owns four consecutive columns of one row and issues
+// the P 16-byte loads before summing them.
+#include "tp_internal.h"
+
+namespace tpl {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+template <bool OUT_BF16, bool HAS_BIAS>
+__global__ __launch_bounds__(kThreads) void combine_sum_kernel(SumProblem a)
+{
+    const int64_t ng = (a.N + 3) >> 2;  // 4-column groups per row
+    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (g >= ng)
+        return;
+    const int64_t c = g * 4;
+    for (int64_t row = blockIdx.y; row < a.M; row += gridDim.y) {
+        const int64_t off = row * a.ld_part + c;
+        if (c + 4 <= a.N) {
+            f32x4 v[kMaxParts];
+#pragma unroll
+            for (int p = 0; p < kMaxParts; ++p)
+                if (p < a.num_parts)
+                    v[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.parts[p] + off));
+            f32x4 s = v[0];
+#pragma unroll
+            for (int p = 1; p < kMaxParts; ++p)
+                if (p < a.num_parts)
+                    s = s + v[p];
+            if (HAS_BIAS) {
+                const bf16x4 b = *reinterpret_cast<const bf16x4 *>(a.bias + c);
+                s = s + f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+            }
+            const int64_t o = row * a.ld_out + c;
+            if (OUT_BF16) {
+                const bf16x4 r = bf16x4{(__bf16)s[0], (__bf16)s[1], (__bf16)s[2], (__bf16)s[3]};
+                *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint16_t *>(a.out) + o) = r;
+            } else {
+                *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + o) = s;
+            }
+        } else {
+            for (int64_t cc = c; cc < a.N; ++cc) {
+                float s = a.parts[0][row * a.ld_part + cc];
+                for (int p = 1; p < a.num_parts; ++p)
+                    s = s + a.parts[p][row * a.ld_part + cc];
+                if (HAS_BIAS)
+                    s = s + (float)(*reinterpret_cast<const __bf16 *>(a.bias + cc));
+                const int64_t o = row * a.ld_out + cc;
+                if (OUT_BF16)
+                    *reinterpret_cast<__bf16 *>(reinterpret_cast<uint16_t *>(a.out) + o) = (__bf16)s;
+                else
+                    reinterpret_cast<float *>(a.out)[o] = s;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine_sum(const SumProblem &p, hipStream_t stream)
+{
+    const int64_t ng = (p.N + 3) / 4;
+    const unsigned gx = (unsigned)((ng + kThreads - 1) / kThreads);
+    const unsigned gy = (unsigned)(p.M < 65535 ? p.M : 65535);
+    const dim3 grid(gx, gy);
+    const dim3 block(kThreads);
+    const bool bias = p.bias != nullptr;
+    if (p.out_bf16) {
+        if (bias)
+            hipLaunchKernelGGL((combine_sum_kernel<true, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((combine_sum_kernel<true, false>), grid, block, 0, stream, p);
+    } else {
+        if (bias)
+            hipLaunchKernelGGL((combine_sum_kernel<false, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((combine_sum_kernel<false, false>), grid, block, 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tpl

@@ -1,0 +1,62 @@
+// tp_internal.h -- declarations shared by the kernel files and the C-ABI layer
+// of libtp_linear.so.  Everything here is internal; the public contract is
+// include/tp_linear.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpl {
+
+// Problem description of one linear-layer launch: Y = epilogue(X . W^T).
+// X [M, K] bf16 (row stride ldx), W [N, K] bf16 (row stride ldw), Y [M, N]
+// (row stride ldy) in bf16 or fp32, optional bias [N] bf16, optional GELU-tanh.
+struct LinearProblem {
+    const uint16_t *x;
+    int64_t ldx;
+    const uint16_t *w;
+    int64_t ldw;
+    const uint16_t *bias;  // nullptr: no bias
+    void *y;
+    int64_t ldy;
+    int64_t M, N, K;
+    bool out_bf16;
+    bool gelu;
+};
+
+// Tiled MFMA GEMM (M > kSkinnyMaxM).  Requires K % 64 == 0, N % 16 == 0.
+hipError_t launch_gemm(const LinearProblem &p, hipStream_t stream);
+
+// Weight-streaming kernel for M <= kSkinnyMaxM (skinny adaLN modulation shape).
+constexpr int64_t kSkinnyMaxM = 16;
+// Bytes of LDS the skinny kernel may use to stage the activation rows.
+constexpr int64_t kSkinnyMaxLdsBytes = 96 * 1024;
+hipError_t launch_gemv(const LinearProblem &p, hipStream_t stream);
+
+// Bit-exact strided copies: `rows` rows of `row_bytes` bytes each.
+struct CopySegment {
+    const char *src;
+    char *dst;
+    int64_t src_ld;  // bytes between source rows
+    int64_t dst_ld;  // bytes between destination rows
+    int64_t rows;
+    int64_t row_bytes;
+};
+constexpr int kMaxSegmentsPerLaunch = 32;
+hipError_t launch_copy_segments(const CopySegment *segs, int nseg, hipStream_t stream);
+
+// SUM combine: out = ((p0 + p1) + ... ) + bias, fp32 adds, fp32 or bf16 out.
+constexpr int kMaxParts = 16;
+struct SumProblem {
+    const float *parts[kMaxParts];
+    int num_parts;
+    int64_t ld_part;  // elements
+    void *out;
+    int64_t ld_out;   // elements
+    const uint16_t *bias;
+    int64_t M, N;
+    bool out_bf16;
+};
+hipError_t launch_combine_sum(const SumProblem &p, hipStream_t stream);
+
+}  // namespace tpl

@@ -1,0 +1,234 @@
+"""Host-side tests of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments before any device work.  CPU only: no call here
+reaches a kernel launch (every call fails validation, is a shape query, or is
+an M == 0 no-op).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import tensor_sharded_linear_amd as tsl
+from tensor_sharded_linear_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp_linear.h")
+
+# Fake, well-aligned device addresses: validation never dereferences them.
+A = 0x7F0000000000
+A2 = 0x7F0000100000
+A3 = 0x7F0000200000
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(tp_[a-z_]+)\s*\(", text))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = tsl.load_library()
+    syms = declared_symbols()
+    assert syms == {"tp_linear_colwise", "tp_linear_rowwise", "tp_fused_qkv_split",
+                    "tp_partial_combine", "tp_plan_shard_slice", "tp_last_error"}
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert set(B.SIGNATURES) == syms
+
+
+def test_nm_shows_extern_c_symbols():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", tsl.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    names = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for s in declared_symbols():
+        assert s in names, s
+
+
+def _call(name, *args):
+    lib = tsl.load_library()
+    return getattr(lib, name)(*args)
+
+
+def colwise(**kw):
+    a = dict(x=A, ldx=256, w=A2, ldw=256, bias=None, y=A3, ldy=512, y_dtype=B.TP_BF16,
+             act=B.TP_ACT_NONE, M=64, N=512, K=256, stream=None)
+    a.update(kw)
+    return _call("tp_linear_colwise", *a.values())
+
+
+def rowwise(**kw):
+    a = dict(x=A, ldx=512, w=A2, ldw=512, p=A3, ldp=256, M=64, N=256, K=512, stream=None)
+    a.update(kw)
+    return _call("tp_linear_rowwise", *a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=100), B.TP_ERR_UNSUPPORTED),
+    (dict(N=500), B.TP_ERR_UNSUPPORTED),
+    (dict(M=-1), B.TP_ERR_INVALID_ARG),
+    (dict(N=0), B.TP_ERR_INVALID_ARG),
+    (dict(ldx=128), B.TP_ERR_INVALID_ARG),
+    (dict(ldx=260), B.TP_ERR_INVALID_ARG),
+    (dict(ldw=200), B.TP_ERR_INVALID_ARG),
+    (dict(ldy=500), B.TP_ERR_INVALID_ARG),
+    (dict(x=None), B.TP_ERR_INVALID_ARG),
+    (dict(w=None), B.TP_ERR_INVALID_ARG),
+    (dict(y=None), B.TP_ERR_INVALID_ARG),
+    (dict(x=A + 2), B.TP_ERR_INVALID_ARG),
+    (dict(bias=A + 4), B.TP_ERR_INVALID_ARG),
+    (dict(y_dtype=7), B.TP_ERR_INVALID_ARG),
+    (dict(act=3), B.TP_ERR_INVALID_ARG),
+    (dict(K=(1 << 31)), B.TP_ERR_UNSUPPORTED),
+])
+def test_colwise_validation(kw, status):
+    assert colwise(**kw) == status
+    assert tsl.tp_last_error().startswith("tp_linear_colwise")
+
+
+def test_colwise_and_rowwise_empty_is_noop():
+    assert colwise(M=0, x=None, y=None) == B.TP_OK
+    assert rowwise(M=0, x=None, p=None) == B.TP_OK
+    assert tsl.tp_last_error() == ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=96), B.TP_ERR_UNSUPPORTED),
+    (dict(N=250), B.TP_ERR_UNSUPPORTED),
+    (dict(ldp=258), B.TP_ERR_INVALID_ARG),
+    (dict(ldp=128), B.TP_ERR_INVALID_ARG),
+    (dict(ldx=500), B.TP_ERR_INVALID_ARG),
+    (dict(p=A3 + 8), B.TP_ERR_INVALID_ARG),
+])
+def test_rowwise_validation(kw, status):
+    assert rowwise(**kw) == status
+
+
+def qkv(**kw):
+    a = dict(w=A, b=None, ws=A2, bs=None, H=24, hd=128, K=3072, dtype=B.TP_BF16, P=4, r=0,
+             stream=None)
+    a.update(kw)
+    return _call("tp_fused_qkv_split", *a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=5), B.TP_ERR_NOT_DIVISIBLE),      # 5 does not divide 24 heads
+    (dict(P=0), B.TP_ERR_INVALID_ARG),
+    (dict(r=4), B.TP_ERR_INVALID_ARG),
+    (dict(r=-1), B.TP_ERR_INVALID_ARG),
+    (dict(H=0), B.TP_ERR_INVALID_ARG),
+    (dict(b=A3), B.TP_ERR_INVALID_ARG),       # bias in without bias out
+    (dict(w=None), B.TP_ERR_INVALID_ARG),
+    (dict(dtype=9), B.TP_ERR_INVALID_ARG),
+])
+def test_qkv_split_validation(kw, status):
+    assert qkv(**kw) == status
+
+
+def test_qkv_divisibility_matches_oracle():
+    for heads in (1, 5, 6, 24, 48):
+        for P in range(1, 10):
+            st = qkv(H=heads, P=P, hd=2, K=8, w=None)  # null weight: only divisibility can pass first
+            try:
+                oracle.check_plan("qkv", P, 0, 3 * heads * 2, 8, num_heads=heads)
+                want = B.TP_ERR_INVALID_ARG   # plan fine, then the null pointer is rejected
+            except oracle.PlanError:
+                want = B.TP_ERR_NOT_DIVISIBLE
+            assert st == want, (heads, P)
+
+
+def shape_query(o, i, style, P, r, blocks=None):
+    return tsl.tp_plan_shard_shape(o, i, style, P, r, blocks)
+
+
+@pytest.mark.parametrize("o,i,style,P,blocks", [
+    (1024, 256, "colwise", 2, None), (256, 1024, "rowwise", 2, None),
+    (9216, 3072, "colwise", 4, [1, 1, 1]), (18432, 6144, "colwise", 8, [1, 1, 1]),
+    (6144, 18432, "rowwise", 8, None), (36864, 6144, "colwise", 4, None),
+    (18, 4, "colwise", 2, [1, 1, 1, 3, 3]), (8, 4, "colwise", 4, [1, 3]),
+    (8, 4, "colwise", 3, None), (4, 9, "rowwise", 2, None), (8, 4, "colwise", 1, [1, 1, 1]),
+    (8, 6, "rowwise", 2, [1, 2]), (24, 8, "rowwise", 2, [1, 1, 1, 3, 3]),
+])
+def test_shard_shape_query_agrees_with_oracle_plan_rules(o, i, style, P, blocks):
+    try:
+        oracle.check_plan(style, P, 0, o, i, blocks=blocks)
+        ok = True
+    except oracle.PlanError:
+        ok = False
+    if ok:
+        rows, cols = shape_query(o, i, style, P, 0, blocks)
+        assert (rows, cols) == ((o // P, i) if style == "colwise" else (o, i // P))
+    else:
+        with pytest.raises(ValueError) as e:
+            shape_query(o, i, style, P, 0, blocks)
+        assert e.value.status == B.TP_ERR_NOT_DIVISIBLE
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(P=0), B.TP_ERR_INVALID_ARG), (dict(r=2), B.TP_ERR_INVALID_ARG),
+    (dict(style=5), B.TP_ERR_INVALID_ARG), (dict(dtype=3), B.TP_ERR_INVALID_ARG),
+    (dict(o=0), B.TP_ERR_INVALID_ARG), (dict(blocks=[0, 1]), B.TP_ERR_INVALID_ARG),
+    (dict(blocks=[1] * 17), B.TP_ERR_INVALID_ARG),
+    (dict(style=B.TP_ROWWISE, b=A3, bs=A3 + 64), B.TP_ERR_INVALID_ARG),
+    (dict(b=A3), B.TP_ERR_INVALID_ARG), (dict(w=None), B.TP_ERR_INVALID_ARG),
+])
+def test_shard_slice_validation(args, status):
+    a = dict(w=A, b=None, ws=A2, bs=None, o=64, i=32, dtype=B.TP_BF16, style=B.TP_COLWISE,
+             blocks=None, P=2, r=0)
+    a.update(args)
+    bl = a.pop("blocks")
+    arr = None if bl is None else (ctypes.c_int64 * len(bl))(*bl)
+    r_, c_ = ctypes.c_int64(), ctypes.c_int64()
+    st = _call("tp_plan_shard_slice", a["w"], a["b"], a["ws"], a["bs"], a["o"], a["i"], a["dtype"],
+               a["style"], arr, 0 if bl is None else len(bl), a["P"], a["r"], ctypes.byref(r_),
+               ctypes.byref(c_), None)
+    assert st == status
+
+
+def combine(parts, mode=B.TP_COMBINE_SUM, **kw):
+    a = dict(ld_part=256, out=A3, ld_out=256, in_dtype=B.TP_F32, out_dtype=B.TP_F32, mode=mode,
+             bias=None, blocks=None, nb=0, M=64, n=256, stream=None)
+    a.update(kw)
+    arr = (ctypes.c_void_p * max(len(parts), 1))(*parts) if parts is not None else None
+    bl = a.pop("blocks")
+    blarr = None if bl is None else (ctypes.c_int64 * len(bl))(*bl)
+    return _call("tp_partial_combine", arr, len(parts or []), a["ld_part"], a["out"], a["ld_out"],
+                 a["in_dtype"], a["out_dtype"], a["mode"], a["bias"], blarr, a["nb"], a["M"], a["n"],
+                 a["stream"])
+
+
+def test_combine_validation():
+    two = [A, A2]
+    assert combine([]) == B.TP_ERR_INVALID_ARG
+    assert combine([A] * 17) == B.TP_ERR_INVALID_ARG
+    assert combine(two, in_dtype=B.TP_BF16) == B.TP_ERR_INVALID_ARG
+    assert combine(two, ld_part=100) == B.TP_ERR_INVALID_ARG
+    assert combine(two, ld_out=100) == B.TP_ERR_INVALID_ARG
+    assert combine(two, blocks=[1], nb=1) == B.TP_ERR_INVALID_ARG
+    assert combine([A, A2 + 4]) == B.TP_ERR_INVALID_ARG
+    assert combine(two, out=A2) == B.TP_ERR_INVALID_ARG          # out aliases parts[1]
+    assert combine(two, out=A, out_dtype=B.TP_BF16) == B.TP_ERR_INVALID_ARG  # bf16 in place
+    assert combine(two, mode=9) == B.TP_ERR_INVALID_ARG
+    assert combine(two, M=0) == B.TP_OK
+    # concat
+    cc = dict(mode=B.TP_COMBINE_CONCAT, in_dtype=B.TP_BF16, out_dtype=B.TP_BF16, ld_out=512)
+    assert combine(two, **cc, M=0) == B.TP_OK
+    assert combine(two, **dict(cc, out_dtype=B.TP_F32)) == B.TP_ERR_INVALID_ARG
+    assert combine(two, **dict(cc, ld_out=500)) == B.TP_ERR_INVALID_ARG
+    assert combine(two, **cc, bias=A3) == B.TP_ERR_INVALID_ARG
+    # packed blocks: [1,3] over 512 columns with 2 parts -> 128 and 384, each divisible by 2: ok
+    assert combine(two, **cc, blocks=[1, 3], nb=2, M=0) == B.TP_OK
+    # [1,1,1] does not divide 512
+    assert combine(two, **cc, blocks=[1, 1, 1], nb=3) == B.TP_ERR_NOT_DIVISIBLE
+    # 4 parts of 2 columns: blocks [1,3] -> sizes 2 and 6, not divisible by 4
+    assert combine([A] * 4, **dict(cc, ld_part=8, ld_out=8, n=2), blocks=[1, 3], nb=2) == \
+        B.TP_ERR_NOT_DIVISIBLE
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        tsl.tp_linear_colwise(x, x)

@@ -1,0 +1,149 @@
+"""GPU parity of the colwise / rowwise GEMMs (tiled MFMA kernel and the skinny
+weight-streaming kernel) against the oracle, through the C ABI.
+
+Ragged shapes span several 256x256 tiles with partial tiles on both edges.
+Integer-valued inputs make every summation order exact, so there the GPU must
+equal the oracle bit for bit, which pins operand layout and indexing; random
+inputs are held to the stated tolerance and to the derived per-element bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+import tensor_sharded_linear_amd as tsl
+from helpers import abs_dot, bits_to_dev, check_close, dev_to_f64
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [(1, 16, 64), (17, 48, 128), (255, 272, 320), (257, 512, 256), (300, 784, 576),
+          (64, 512, 256), (513, 256, 1024), (16, 1024, 192), (5, 80, 6144)]
+
+
+@pytest.mark.parametrize("M,N,K", RAGGED)
+def test_colwise_integer_inputs_exact(M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    x = si.int_bf16(rng, (M, K), -4, 4)
+    w = si.int_bf16(rng, (N, K), -4, 4)
+    b = si.int_bf16(rng, (N,), -8, 8)
+    y = tsl.tp_linear_colwise(bits_to_dev(x), bits_to_dev(w), bits_to_dev(b), out_dtype=torch.float32)
+    ref = oracle.colwise(x, w, b)
+    assert np.array_equal(dev_to_f64(y), ref)
+
+
+@pytest.mark.parametrize("M,N,K", RAGGED)
+def test_rowwise_integer_inputs_exact(M, N, K):
+    rng = np.random.default_rng(7 * M + N + K)
+    P = 2
+    x = si.int_bf16(rng, (M, 2 * K), -4, 4)
+    w = si.int_bf16(rng, (N, 2 * K), -4, 4)
+    xd, wd = bits_to_dev(x), bits_to_dev(w)
+    for r in range(P):
+        ws, _ = tsl.tp_plan_shard_slice(wd, None, "rowwise", P, r)
+        p = tsl.tp_linear_rowwise(xd[:, r * K:(r + 1) * K], ws)  # strided input slice, ldx = 2K
+        ref = oracle.rowwise(x, r, P, oracle.shard_rowwise(w, P, r))
+        assert np.array_equal(dev_to_f64(p), ref)
+
+
+@pytest.mark.parametrize("M,N,K", RAGGED)
+@pytest.mark.parametrize("act", ["none", "gelu_tanh"])
+def test_colwise_random_bf16_out(M, N, K, act):
+    rng = np.random.default_rng(3 * M + N + 5 * K)
+    x = si.normal_bf16(rng, (M, K))
+    w = si.normal_bf16(rng, (N, K), 1 / np.sqrt(K))
+    b = si.normal_bf16(rng, (N,))
+    y = tsl.tp_linear_colwise(bits_to_dev(x), bits_to_dev(w), bits_to_dev(b), act=act)
+    a = oracle.ACT_GELU_TANH if act == "gelu_tanh" else oracle.ACT_NONE
+    ref = oracle.colwise(x, w, b, act=a)
+    check_close(dev_to_f64(y), ref, K, True, S=abs_dot(x, w, b), what=f"colwise {M}x{N}x{K} {act}")
+
+
+@pytest.mark.parametrize("M,N,K", RAGGED)
+def test_rowwise_random_f32_partial(M, N, K):
+    rng = np.random.default_rng(11 * M + N + K)
+    x = si.normal_bf16(rng, (M, K))
+    w = si.normal_bf16(rng, (N, K), 1 / np.sqrt(K))
+    p = tsl.tp_linear_rowwise(bits_to_dev(x), bits_to_dev(w))
+    ref = oracle.linear(x, w)
+    check_close(dev_to_f64(p), ref, K, False, S=abs_dot(x, w), what=f"rowwise {M}x{N}x{K}")
+
+
+def test_colwise_f32_out_with_gelu_and_padded_strides():
+    rng = np.random.default_rng(99)
+    M, N, K = 200, 96, 128
+    xb = si.normal_bf16(rng, (M, K + 64))
+    wb = si.normal_bf16(rng, (N, K + 32), 1 / np.sqrt(K))
+    x = bits_to_dev(xb)[:, 64:]          # ldx = K + 64, offset 128 bytes
+    w = bits_to_dev(wb)[:, :K]           # ldw = K + 32
+    out_big = torch.full((M, N + 16), 7.0, dtype=torch.float32, device="cuda")
+    out = out_big[:, :N]
+    tsl.tp_linear_colwise(x, w, act="gelu_tanh", out=out)
+    ref = oracle.colwise(np.ascontiguousarray(xb[:, 64:]), np.ascontiguousarray(wb[:, :K]),
+                         act=oracle.ACT_GELU_TANH)
+    check_close(dev_to_f64(out), ref, K, False, what="colwise f32 gelu strided")
+    assert torch.all(out_big[:, N:] == 7.0)
+
+
+def test_empty_m_is_noop():
+    w = torch.zeros(64, 128, dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros(0, 128, dtype=torch.bfloat16, device="cuda")
+    y = tsl.tp_linear_colwise(x, w)
+    assert y.shape == (0, 64)
+    p = tsl.tp_linear_rowwise(x, w)
+    assert p.shape == (0, 64)
+
+
+@pytest.mark.parametrize("P", [2, 4])
+def test_concat_of_colwise_shards_equals_unsharded_gpu(P):
+    """[TP] opening definition, on the GPU alone: the colwise shards' outputs, gathered,
+    equal the unsharded layer bit for bit (each output element's arithmetic does not
+    depend on the sharding)."""
+    rng = np.random.default_rng(P)
+    M, N, K = 600, 1024, 512
+    x = bits_to_dev(si.normal_bf16(rng, (M, K)))
+    w = bits_to_dev(si.normal_bf16(rng, (N, K), 1 / np.sqrt(K)))
+    b = bits_to_dev(si.normal_bf16(rng, (N,)))
+    full = tsl.tp_linear_colwise(x, w, b, act="gelu_tanh")
+    outs = []
+    for r in range(P):
+        ws, bs = tsl.tp_plan_shard_slice(w, b, "colwise", P, r)
+        outs.append(tsl.tp_linear_colwise(x, ws, bs, act="gelu_tanh"))
+    cat = tsl.tp_partial_combine(outs, "concat")
+    assert torch.equal(cat.view(torch.int16), full.view(torch.int16))
+
+
+def test_repeat_runs_are_bitwise_identical():
+    rng = np.random.default_rng(5)
+    M, N, K = 700, 512, 768
+    x = bits_to_dev(si.normal_bf16(rng, (M, K)))
+    w = bits_to_dev(si.normal_bf16(rng, (N, K), 1 / np.sqrt(K)))
+    a = tsl.tp_linear_rowwise(x, w)
+    b = tsl.tp_linear_rowwise(x, w)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 7, 16])
+@pytest.mark.parametrize("act,bias", [("none", False), ("gelu_tanh", True)])
+def test_skinny_path_random(B, act, bias):
+    rng = np.random.default_rng(B)
+    N, K = 528, 1536
+    c = si.normal_bf16(rng, (B, K))
+    w = si.normal_bf16(rng, (N, K), 1 / np.sqrt(K))
+    bb = si.normal_bf16(rng, (N,)) if bias else None
+    y = tsl.tp_linear_colwise(bits_to_dev(c), bits_to_dev(w), bits_to_dev(bb) if bias else None, act=act)
+    a = oracle.ACT_GELU_TANH if act == "gelu_tanh" else oracle.ACT_NONE
+    ref = oracle.colwise(c, w, bb, act=a)
+    check_close(dev_to_f64(y), ref, K, True, S=abs_dot(c, w, bb), what=f"skinny B={B}")
+
+
+@pytest.mark.parametrize("B", [1, 4, 16])
+def test_skinny_path_integer_exact(B):
+    rng = np.random.default_rng(40 + B)
+    N, K = 272, 2048
+    c = si.int_bf16(rng, (B, K), -4, 4)
+    w = si.int_bf16(rng, (N, K), -4, 4)
+    y = tsl.tp_linear_colwise(bits_to_dev(c), bits_to_dev(w), out_dtype=torch.float32)
+    assert np.array_equal(dev_to_f64(y), oracle.colwise(c, w))
+    p = tsl.tp_linear_rowwise(bits_to_dev(c), bits_to_dev(w))
+    assert np.array_equal(dev_to_f64(p), oracle.linear(c, w))
