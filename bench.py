@@ -1,0 +1,343 @@
+"""Benchmark: one rank's share of tensor-parallel DiT linear layers, every rank in turn, on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+
+  full block (hidden 6144, 48 heads x 128, FFN 18432, 4608 tokens), for each
+  tp degree P in {2, 4, 8}:
+    * shard every weight for every rank: head-aligned fused-QKV split,
+      out-proj rowwise, FFN-up colwise, FFN-down rowwise (index kernels);
+    * every rank: colwise QKV, rowwise out-proj (fp32 partial), colwise
+      FFN-up + GELU-tanh, rowwise FFN-down (fp32 partial);
+    * layer-boundary combines: SUM of the out-proj partials (fp32) and of the
+      FFN-down partials (bf16 out), CONCAT of the QKV outputs (packed [1,1,1])
+      and of the FFN-up outputs;
+  adaLN modulation (6144 -> 36864, colwise P=4, 4 conditioning rows): shard
+  the weight for the 4 ranks, then each rank's skinny weight-streaming GEMV.
+
+Inputs are seeded synthetic bf16 tensors already resident in HBM when the timed
+region starts.  `value` is the step's sharded-linear TFLOP/s (all GEMM and GEMV
+flops / wall time per step).  Per-kernel durations come from HIP events around
+every launch of the timed steps, on the stream the library launches on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+GEMM_SRC = os.path.join(ROOT, "tensor_sharded_linear_amd", "csrc", "gemm_bf16.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--tp", type=str, default="2,4,8", help="tp degrees of the full block")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--detail", action="store_true", help="also print a per-shape GEMM table to stderr")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events around launches on torch's current stream (the library's stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.on = False
+        self.rec = []  # (category, key, work, bytes, ev0, ev1)
+
+    def run(self, cat, key, flops, nbytes, fn):
+        if not self.on:
+            return fn()
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        out = fn()
+        e1.record()
+        self.rec.append((cat, key, flops, nbytes, e0, e1))
+        return out
+
+    def summary(self):
+        cats = {}
+        shapes = {}
+        for cat, key, flops, nbytes, e0, e1 in self.rec:
+            ms = e0.elapsed_time(e1)
+            c = cats.setdefault(cat, dict(ms=0.0, flops=0.0, bytes=0.0, launches=0))
+            c["ms"] += ms
+            c["flops"] += flops
+            c["bytes"] += nbytes
+            c["launches"] += 1
+            if cat == "gemm":
+                s = shapes.setdefault(key, dict(ms=0.0, flops=0.0, launches=0))
+                s["ms"] += ms
+                s["flops"] += flops
+                s["launches"] += 1
+        return cats, shapes
+
+
+def file_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU's share on one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) "
+              "is not supported: the multi-GPU path (RCCL collectives) is not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth_inputs as si
+    import tensor_sharded_linear_amd as tsl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tsl.load_library()
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t_gen = time.time()
+    fb = si.workload("full_block")
+    ada = si.workload("adaln")
+    m = fb.meta
+    M, hidden, ffn, H, hd = m["M"], m["hidden"], m["ffn"], m["heads"], m["head_dim"]
+    x, A = up(fb.arrays["x"]), up(fb.arrays["a"])
+    wqkv, wo = up(fb.arrays["w_qkv"]), up(fb.arrays["w_o"])
+    w1, w2 = up(fb.arrays["w1"]), up(fb.arrays["w2"])
+    c_ada, w_ada = up(ada.arrays["c"]), up(ada.arrays["w_ada"])
+    del fb, ada
+    si.workload.cache_clear()
+    print(f"# inputs generated and uploaded in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    tps = [int(p) for p in args.tp.split(",")]
+    B_ADA, P_ADA = 4, 4
+    n_ada = w_ada.shape[0] // P_ADA
+
+    # Preallocated shards and outputs (per tp degree, per rank).
+    bufs = {}
+    for P in tps:
+        b = dict(
+            wq=[torch.empty(3 * H // P * hd, hidden, dtype=torch.bfloat16, device=dev) for _ in range(P)],
+            wo=[torch.empty(hidden, hidden // P, dtype=torch.bfloat16, device=dev) for _ in range(P)],
+            w1=[torch.empty(ffn // P, hidden, dtype=torch.bfloat16, device=dev) for _ in range(P)],
+            w2=[torch.empty(hidden, ffn // P, dtype=torch.bfloat16, device=dev) for _ in range(P)],
+            q=[torch.empty(M, 3 * H // P * hd, dtype=torch.bfloat16, device=dev) for _ in range(P)],
+            h=[torch.empty(M, ffn // P, dtype=torch.bfloat16, device=dev) for _ in range(P)],
+            po=[torch.empty(M, hidden, dtype=torch.float32, device=dev) for _ in range(P)],
+            pd=[torch.empty(M, hidden, dtype=torch.float32, device=dev) for _ in range(P)],
+            out_sum=torch.empty(M, hidden, dtype=torch.float32, device=dev),
+            down_sum=torch.empty(M, hidden, dtype=torch.bfloat16, device=dev),
+            q_cat=torch.empty(M, 3 * H * hd, dtype=torch.bfloat16, device=dev),
+            h_cat=torch.empty(M, ffn, dtype=torch.bfloat16, device=dev),
+        )
+        bufs[P] = b
+    ada_w = [torch.empty(n_ada, hidden, dtype=torch.bfloat16, device=dev) for _ in range(P_ADA)]
+    ada_y = [torch.empty(B_ADA, n_ada, dtype=torch.bfloat16, device=dev) for _ in range(P_ADA)]
+
+    T = Timer(torch)
+    gemm_flops_step = 0.0
+
+    def gemm_cost(m_, n_, k_, out_es):
+        return 2.0 * m_ * n_ * k_, 2.0 * (m_ * k_ + n_ * k_) + out_es * m_ * n_
+
+    def step():
+        for P in tps:
+            b = bufs[P]
+            kq = 3 * H // P * hd
+            # shard every weight for every rank (index kernels)
+            for r in range(P):
+                T.run("slice", "qkv", 0, 2 * 2 * kq * hidden,
+                      lambda: tsl.tp_fused_qkv_split(wqkv, None, H, hd, P, r, w_out=b["wq"][r]))
+                T.run("slice", "wo", 0, 2 * 2 * hidden * hidden // P,
+                      lambda: tsl.tp_plan_shard_slice(wo, None, "rowwise", P, r, w_out=b["wo"][r]))
+                T.run("slice", "w1", 0, 2 * 2 * ffn // P * hidden,
+                      lambda: tsl.tp_plan_shard_slice(w1, None, "colwise", P, r, w_out=b["w1"][r]))
+                T.run("slice", "w2", 0, 2 * 2 * hidden * ffn // P,
+                      lambda: tsl.tp_plan_shard_slice(w2, None, "rowwise", P, r, w_out=b["w2"][r]))
+            # every rank's projections
+            k_loc = hidden // P
+            for r in range(P):
+                f, by = gemm_cost(M, kq, hidden, 2)
+                T.run("gemm", f"colwise {M}x{kq}x{hidden}", f, by,
+                      lambda: tsl.tp_linear_colwise(x, b["wq"][r], out=b["q"][r]))
+                f, by = gemm_cost(M, hidden, k_loc, 4)
+                T.run("gemm", f"rowwise {M}x{hidden}x{k_loc}", f, by,
+                      lambda: tsl.tp_linear_rowwise(A[:, r * k_loc:(r + 1) * k_loc], b["wo"][r],
+                                                    out=b["po"][r]))
+                f, by = gemm_cost(M, ffn // P, hidden, 2)
+                T.run("gemm", f"colwise+gelu {M}x{ffn // P}x{hidden}", f, by,
+                      lambda: tsl.tp_linear_colwise(x, b["w1"][r], act="gelu_tanh", out=b["h"][r]))
+                f, by = gemm_cost(M, hidden, ffn // P, 4)
+                T.run("gemm", f"rowwise {M}x{hidden}x{ffn // P}", f, by,
+                      lambda: tsl.tp_linear_rowwise(b["h"][r], b["w2"][r], out=b["pd"][r]))
+            # layer-boundary combines
+            T.run("sum", f"P{P} f32", 0, (P + 1) * 4.0 * M * hidden,
+                  lambda: tsl.tp_partial_combine(b["po"], "sum", out=b["out_sum"]))
+            T.run("sum", f"P{P} bf16", 0, (P * 4.0 + 2.0) * M * hidden,
+                  lambda: tsl.tp_partial_combine(b["pd"], "sum", out=b["down_sum"]))
+            T.run("concat", "qkv", 0, 2 * 2.0 * M * 3 * H * hd,
+                  lambda: tsl.tp_partial_combine(b["q"], "concat", blocks=[1, 1, 1], out=b["q_cat"]))
+            T.run("concat", "up", 0, 2 * 2.0 * M * ffn,
+                  lambda: tsl.tp_partial_combine(b["h"], "concat", out=b["h_cat"]))
+        # adaLN modulation: shard for 4 ranks, then each rank's skinny GEMV
+        for r in range(P_ADA):
+            T.run("slice", "w_ada", 0, 2 * 2 * n_ada * hidden,
+                  lambda: tsl.tp_plan_shard_slice(w_ada, None, "colwise", P_ADA, r, w_out=ada_w[r]))
+        for r in range(P_ADA):
+            T.run("gemv", f"adaLN B{B_ADA} {n_ada}x{hidden}", 2.0 * B_ADA * n_ada * hidden,
+                  2.0 * n_ada * hidden + 2.0 * B_ADA * (hidden + n_ada),
+                  lambda: tsl.tp_linear_colwise(c_ada, ada_w[r], out=ada_y[r]))
+
+    for P in tps:
+        gemm_flops_step += P * 2.0 * M * hidden * (3 * H // P * hd + ffn // P) + \
+            P * 2.0 * M * hidden * (hidden // P + ffn // P)
+    lin_flops_step = gemm_flops_step + P_ADA * 2.0 * B_ADA * n_ada * hidden
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    T.on = True
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    T.on = False
+    ms_per_step = (t1 - t0) * 1e3 / max(args.steps, 1)
+    cats, shapes = T.summary()
+
+    def gbs(c):
+        return c["bytes"] / (c["ms"] * 1e-3) / 1e9 if c["ms"] > 0 else 0.0
+
+    g = cats["gemm"]
+    gemm_tflops = g["flops"] / (g["ms"] * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_sha") == file_sha(GEMM_SRC):
+            traffic = tr.get("bytes_per_launch")
+    kernels = {}
+    for name, c in cats.items():
+        ent = dict(launches=c["launches"], avg_us=round(c["ms"] * 1e3 / c["launches"], 2))
+        if c["flops"]:
+            tf = c["flops"] / (c["ms"] * 1e-3) / 1e12
+            ent.update(tflops=round(tf, 1), pct_mfma_peak=round(100 * tf / PEAK_BF16_TFLOPS, 1))
+        ent.update(gbs=round(gbs(c), 1), pct_hbm_peak=round(100 * gbs(c) / PEAK_HBM_GBS, 1))
+        kernels[name] = ent
+    result = {
+        "metric": "sharded bf16 linear TFLOP/s (% MFMA peak); combine GB/s (% HBM peak)",
+        "value": round(lin_flops_step / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "DiT block linear set, every rank of tp 2/4/8 in turn (hidden 6144, 48 heads x 128, "
+                        "FFN 18432, 4608 tokens) + adaLN 6144->36864 colwise tp 4, 4 rows",
+            "tokens": M, "hidden": hidden, "ffn": ffn, "heads": H, "head_dim": hd,
+            "tp_degrees": tps, "adaln_rows": B_ADA, "adaln_tp": P_ADA,
+            "parallelism": "tp shares computed sequentially on 1 GPU",
+        },
+        "roofline": {
+            "kernel": "gemm_bf16_nt_kernel",
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "kernels": kernels,
+        "pct_mfma_peak_whole_step": round(100 * lin_flops_step / (ms_per_step * 1e-3) / 1e12
+                                          / PEAK_BF16_TFLOPS, 1),
+    }
+    if args.detail:
+        for k, s in sorted(shapes.items()):
+            tf = s["flops"] / (s["ms"] * 1e-3) / 1e12
+            print(f"# {k:40s} launches={s['launches']:4d} avg_us={s['ms'] * 1e3 / s['launches']:9.1f} "
+                  f"TFLOP/s={tf:8.1f}", file=sys.stderr)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(target_s: float):
+    """The CPU oracle (as it stands) on a bounded row sample of the same step's GEMM work."""
+    import numpy as np
+
+    import oracle
+    import synth_inputs as si
+
+    fb = si.workload("full_block")
+    a, m = fb.arrays, fb.meta
+    M, hidden, ffn, H, hd = m["M"], m["hidden"], m["ffn"], m["heads"], m["head_dim"]
+    threads = oracle.default_threads()
+    P = 4
+    r = 0
+    wq, _ = oracle.qkv_split(a["w_qkv"], None, H, hd, P, r)
+    wo_s = oracle.shard_rowwise(a["w_o"], P, r)
+    w1_s, _ = oracle.shard_colwise(a["w1"], None, P, r)
+    w2_s = oracle.shard_rowwise(a["w2"], P, r)
+    k_loc = hidden // P
+
+    def run(rows):
+        oracle.colwise(a["x"], wq, rows=rows, threads=threads)
+        oracle.rowwise(a["a"], r, P, wo_s, rows=rows, threads=threads)
+        h = oracle.bf16_round(oracle.colwise(a["x"], w1_s, act=oracle.ACT_GELU_TANH, rows=rows,
+                                             threads=threads))
+        oracle.linear(h, w2_s, threads=threads)
+        return len(rows) * 2.0 * (wq.shape[0] * hidden + hidden * k_loc + w1_s.shape[0] * hidden
+                                  + hidden * w2_s.shape[1])
+
+    rng = np.random.default_rng(0)
+    probe = np.sort(rng.choice(M, size=threads, replace=False))
+    t = time.perf_counter()
+    run(probe)
+    dt = time.perf_counter() - t
+    n = int(max(threads, min(M, threads * max(1, round(target_s / max(dt, 1e-3))))))
+    rows = np.sort(rng.choice(M, size=n, replace=False))
+    t = time.perf_counter()
+    flops = run(rows)
+    dt = time.perf_counter() - t
+    return {
+        "value": round(flops / dt / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "seconds": round(dt, 2),
+        "sample": f"{n} of {M} token rows through rank 0 of tp 4 of the full block (QKV colwise, out-proj "
+                  f"rowwise, FFN-up colwise+GELU, FFN-down rowwise); fp64-accumulating C oracle",
+    }
+
+
+if __name__ == "__main__":
+    main()
