@@ -81,7 +81,7 @@ typedef enum { TP_COMBINE_SUM = 0, TP_COMBINE_CONCAT = 1 } tp_combine;
  *
  * Arithmetic: bf16 products, fp32 accumulation (MFMA), bias and activation in
  * fp32, one rounding to y_dtype (round to nearest even for bf16).
- * M <= 16 uses a weight-streaming kernel (the skinny adaLN modulation shape),
+ * Small M (up to 8 rows, K <= 8192) uses a weight-streaming kernel (the skinny adaLN modulation shape),
  * larger M the tiled MFMA kernel; both obey the same contract.
  * Requires K % 64 == 0 and n_shard % 16 == 0 (TP_ERR_UNSUPPORTED otherwise).
  */

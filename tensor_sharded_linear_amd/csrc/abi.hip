@@ -81,7 +81,7 @@ tp_status check_linear(const char *fn, const void *x, int64_t ldx, const void *w
 
 tp_status run_linear(const char *fn, const tpl::LinearProblem &p, hipStream_t stream)
 {
-    const bool skinny = p.M <= tpl::kSkinnyMaxM && p.M * p.K * 2 <= tpl::kSkinnyMaxLdsBytes;
+    const bool skinny = tpl::gemv_supports(p.M, p.K);
     const hipError_t e = skinny ? tpl::launch_gemv(p, stream) : tpl::launch_gemm(p, stream);
     return hip_status(e, fn);
 }

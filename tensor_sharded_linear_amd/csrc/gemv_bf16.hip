@@ -6,13 +6,18 @@
 // standalone projection.  With M of 1..16 the work is a matrix-vector product
 // bound by how fast the weight streams from HBM, so it gets its own kernel:
 //
-//  * the M activation rows are staged once per workgroup in LDS (bf16);
-//  * each wave takes whole weight rows n (grid-stride over rows), the 64 lanes
-//    read consecutive 16-byte chunks of the row (1 KiB per instruction, fully
-//    coalesced), several chunks in flight per lane;
+//  * one persistent 512-thread workgroup per CU stages the M activation rows
+//    in LDS once (bf16, M * K * 2 bytes);
+//  * each wave takes whole weight rows n (strided over all waves of the
+//    grid); its 64 lanes read consecutive 16-byte chunks of the row (1 KiB per
+//    instruction, fully coalesced, non-temporal), the whole row in one batch;
+//  * the loads of the wave's next row are issued before the current row is
+//    reduced, so every wave keeps a row (K * 2 bytes) in flight while it
+//    computes;
 //  * per chunk and activation row, four v_dot2_f32_bf16 accumulate in fp32;
-//  * a butterfly over the 64 lanes reduces each row's M sums; lanes 0..M-1
-//    apply bias / GELU-tanh and store.
+//    a butterfly over the 64 lanes (DPP inside 16-lane rows, shuffles across
+//    rows) reduces each row's M sums, and lanes 0..M-1 apply bias / GELU-tanh
+//    and store.
 #include "tp_internal.h"
 
 namespace tpl {
@@ -21,9 +26,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kUnroll = 6;  // 16-byte chunks in flight per lane per batch
 
 struct GemvParams {
     const uint16_t *x;
@@ -50,117 +54,167 @@ __device__ __forceinline__ float dot8(const bf16x8 &a, const bf16x8 &b, float ac
     return acc;
 }
 
-template <int BMAX, bool OUT_BF16, bool HAS_BIAS, bool GELU>
-__global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(GemvParams p)
+// Sum over the 64 lanes of a wave.  Inside each 16-lane row the butterfly
+// uses DPP lane swizzles (VALU, no LDS round trip): swap neighbours, swap
+// pairs, mirror each 8-lane half, mirror the row.  The two cross-row steps use
+// lane shuffles.  Every lane ends with the total.
+__device__ __forceinline__ float wave_sum(float v)
 {
-    extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [M][K]
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true));
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// NIT = 16-byte chunks per lane per row = ceil(K / 512); B = activation rows.
+// Lanes whose chunk index runs past the row re-read the row's last chunk and
+// pair it with a zero chunk kept after the activations in LDS, so neither the
+// loads nor the dot products branch per lane.  The epilogue options (bias,
+// GELU, output dtype) are uniform runtime flags: they act once per row.
+template <int NIT, int B>
+__global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(GemvParams p, int out_bf16, int gelu)
+{
+    extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [B][K], then 8 zeros
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int nch = p.K >> 3;  // 16-byte chunks per row (K % 64 == 0)
+    constexpr int UB = B >= 8 ? 1 : 8 / B;  // chunks per LDS batch (8 vectors)
 
-    // Stage the activation rows.
-    for (int idx = tid; idx < p.M * nch; idx += kThreads) {
-        const int b = idx / nch;
-        const int c = idx - b * nch;
-        *reinterpret_cast<bf16x8 *>(xs + b * p.K + c * 8) =
-            *reinterpret_cast<const bf16x8 *>(p.x + (int64_t)b * p.ldx + c * 8);
+    auto wch = [&](int u) { return min(u * 64 + lane, nch - 1) * 8; };
+    auto xch = [&](int u) { return u * 64 + lane < nch ? (u * 64 + lane) * 8 : B * p.K; };
+
+    const int stride = gridDim.x * kWaves;
+    int r0 = blockIdx.x * kWaves + wave;
+    bf16x8 ra[NIT], rb[NIT];
+
+#define TPL_LOAD_ROW(n, r)                                                                   \
+    do {                                                                                     \
+        const uint16_t *src_ = p.w + (int64_t)(n) * p.ldw;                                    \
+        _Pragma("unroll") for (int u = 0; u < NIT; ++u)                                      \
+            r[u] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(src_ + wch(u))); \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+    } while (0)
+
+#define TPL_FINISH_ROW(n, r)                                                                 \
+    do {                                                                                     \
+        float acc_[B];                                                                       \
+        _Pragma("unroll") for (int b = 0; b < B; ++b) acc_[b] = 0.f;                         \
+        _Pragma("unroll") for (int u0 = 0; u0 < NIT; u0 += UB) {                             \
+            bf16x8 xv_[UB][B];                                                               \
+            _Pragma("unroll") for (int u = 0; u < UB; ++u)                                   \
+                _Pragma("unroll") for (int b = 0; b < B; ++b)                                \
+                    if (u0 + u < NIT)                                                        \
+                        xv_[u][b] = *reinterpret_cast<const bf16x8 *>(xs + b * p.K + xch(u0 + u)); \
+            _Pragma("unroll") for (int u = 0; u < UB; ++u)                                   \
+                _Pragma("unroll") for (int b = 0; b < B; ++b)                                \
+                    if (u0 + u < NIT)                                                        \
+                        acc_[b] = dot8(r[u0 + u], xv_[u][b], acc_[b]);                        \
+            __builtin_amdgcn_sched_barrier(0);                                               \
+        }                                                                                    \
+        _Pragma("unroll") for (int b = 0; b < B; ++b) acc_[b] = wave_sum(acc_[b]);           \
+        if (lane < B) {                                                                      \
+            float v_ = acc_[0];                                                              \
+            _Pragma("unroll") for (int b = 1; b < B; ++b) if (b == lane) v_ = acc_[b];       \
+            if (p.bias) v_ += (float)(*reinterpret_cast<const __bf16 *>(p.bias + (n)));       \
+            if (gelu) v_ = gelu_tanh(v_);                                                    \
+            if (out_bf16)                                                                    \
+                *reinterpret_cast<__bf16 *>(reinterpret_cast<uint16_t *>(p.y) + (int64_t)lane * p.ldy + (n)) = (__bf16)v_; \
+            else                                                                             \
+                reinterpret_cast<float *>(p.y)[(int64_t)lane * p.ldy + (n)] = v_;            \
+        }                                                                                    \
+    } while (0)
+
+    // Issue this wave's first row before staging the activations.
+    if (r0 < p.N)
+        TPL_LOAD_ROW(r0, ra);
+    for (int idx = tid; idx < B * nch; idx += kThreads) {
+        const int bb = idx / nch;
+        const int c = idx - bb * nch;
+        *reinterpret_cast<bf16x8 *>(xs + bb * p.K + c * 8) =
+            *reinterpret_cast<const bf16x8 *>(p.x + (int64_t)bb * p.ldx + c * 8);
     }
+    if (tid == 0)
+        *reinterpret_cast<bf16x8 *>(xs + B * p.K) = bf16x8{};
     __syncthreads();
 
-    const int wave_stride = gridDim.x * kWaves;
-    for (int n = blockIdx.x * kWaves + wave; n < p.N; n += wave_stride) {
-        const uint16_t *wr = p.w + (int64_t)n * p.ldw;
-        float acc[BMAX];
-#pragma unroll
-        for (int b = 0; b < BMAX; ++b)
-            acc[b] = 0.f;
-        for (int c0 = 0; c0 < nch; c0 += 64 * kUnroll) {
-            bf16x8 wv[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int c = c0 + u * 64 + lane;
-                if (c < nch)
-                    wv[u] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(wr + c * 8));
-            }
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int c = c0 + u * 64 + lane;
-                if (c < nch) {
-#pragma unroll
-                    for (int b = 0; b < BMAX; ++b) {
-                        if (b < p.M) {
-                            const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(xs + b * p.K + c * 8);
-                            acc[b] = dot8(wv[u], xv, acc[b]);
-                        }
-                    }
-                }
-            }
-        }
-        // Butterfly reduction over the wave: every lane ends with the row totals.
-#pragma unroll
-        for (int b = 0; b < BMAX; ++b) {
-            if (b < p.M) {
-#pragma unroll
-                for (int off = 32; off >= 1; off >>= 1)
-                    acc[b] += __shfl_xor(acc[b], off, 64);
-            }
-        }
-        if (lane < p.M) {
-            float v = 0.f;
-#pragma unroll
-            for (int b = 0; b < BMAX; ++b)
-                if (b == lane)
-                    v = acc[b];
-            if (HAS_BIAS)
-                v += (float)(*reinterpret_cast<const __bf16 *>(p.bias + n));
-            if (GELU)
-                v = gelu_tanh(v);
-            if (OUT_BF16)
-                *reinterpret_cast<__bf16 *>(reinterpret_cast<uint16_t *>(p.y) + (int64_t)lane * p.ldy + n) = (__bf16)v;
-            else
-                reinterpret_cast<float *>(p.y)[(int64_t)lane * p.ldy + n] = v;
-        }
+    // Two rows in flight per wave: A is reduced while B loads, and back.
+    while (r0 < p.N) {
+        const int r1 = r0 + stride;
+        if (r1 < p.N)
+            TPL_LOAD_ROW(r1, rb);
+        TPL_FINISH_ROW(r0, ra);
+        if (r1 >= p.N)
+            break;
+        const int r2 = r1 + stride;
+        if (r2 < p.N)
+            TPL_LOAD_ROW(r2, ra);
+        TPL_FINISH_ROW(r1, rb);
+        r0 = r2;
     }
+#undef TPL_LOAD_ROW
+#undef TPL_FINISH_ROW
 }
 
-template <int BMAX, bool OUT_BF16, bool HAS_BIAS, bool GELU>
-hipError_t launch_variant(const GemvParams &gp, hipStream_t stream)
+template <int NIT, int B>
+hipError_t launch_variant(const GemvParams &gp, bool out_bf16, bool gelu, hipStream_t stream)
 {
-    const size_t lds = (size_t)gp.M * gp.K * sizeof(uint16_t);
-    auto kern = gemv_bf16_kernel<BMAX, OUT_BF16, HAS_BIAS, GELU>;
+    const size_t lds = ((size_t)B * gp.K + 8) * sizeof(uint16_t);
+    auto kern = gemv_bf16_kernel<NIT, B>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess)
             return e;
     }
+    // One persistent workgroup per CU (256 CUs), fewer if there are fewer rows.
     int blocks = (gp.N + kWaves - 1) / kWaves;
-    // Persistent-style grid: a few workgroups per CU, rows strided over waves,
-    // so the activation rows are staged into LDS only a few times per CU.
-    const int cap = 256 * 2;
-    if (blocks > cap)
-        blocks = cap;
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, stream, gp);
+    if (blocks > 256)
+        blocks = 256;
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, stream, gp, (int)out_bf16, (int)gelu);
     return hipGetLastError();
 }
 
-template <int BMAX>
-hipError_t launch_bmax(const GemvParams &gp, bool out_bf16, bool bias, bool gelu, hipStream_t s)
+// Largest row count whose row buffers + activation batch fit the 256-register
+// budget of two waves per SIMD without spilling, per chunk count.
+constexpr int max_rows(int nit) { return nit <= 8 ? 8 : (nit <= 12 ? 7 : 3); }
+
+int chunk_iters(int64_t K) { return (int)((K / 8 + 63) / 64); }
+
+template <int NIT, int B>
+hipError_t launch_if_fits(const GemvParams &gp, bool out_bf16, bool gelu, hipStream_t s)
 {
-    const int sel = (out_bf16 ? 4 : 0) | (bias ? 2 : 0) | (gelu ? 1 : 0);
-    switch (sel) {
-    case 0: return launch_variant<BMAX, false, false, false>(gp, s);
-    case 1: return launch_variant<BMAX, false, false, true>(gp, s);
-    case 2: return launch_variant<BMAX, false, true, false>(gp, s);
-    case 3: return launch_variant<BMAX, false, true, true>(gp, s);
-    case 4: return launch_variant<BMAX, true, false, false>(gp, s);
-    case 5: return launch_variant<BMAX, true, false, true>(gp, s);
-    case 6: return launch_variant<BMAX, true, true, false>(gp, s);
-    default: return launch_variant<BMAX, true, true, true>(gp, s);
+    if constexpr (B <= max_rows(NIT))
+        return launch_variant<NIT, B>(gp, out_bf16, gelu, s);
+    return hipErrorInvalidValue;  // excluded by gemv_supports()
+}
+
+template <int NIT>
+hipError_t launch_rows(const GemvParams &gp, bool out_bf16, bool gelu, hipStream_t s)
+{
+    switch (gp.M) {
+    case 1: return launch_if_fits<NIT, 1>(gp, out_bf16, gelu, s);
+    case 2: return launch_if_fits<NIT, 2>(gp, out_bf16, gelu, s);
+    case 3: return launch_if_fits<NIT, 3>(gp, out_bf16, gelu, s);
+    case 4: return launch_if_fits<NIT, 4>(gp, out_bf16, gelu, s);
+    case 5: return launch_if_fits<NIT, 5>(gp, out_bf16, gelu, s);
+    case 6: return launch_if_fits<NIT, 6>(gp, out_bf16, gelu, s);
+    case 7: return launch_if_fits<NIT, 7>(gp, out_bf16, gelu, s);
+    default: return launch_if_fits<NIT, 8>(gp, out_bf16, gelu, s);
     }
 }
 
 }  // namespace
+
+bool gemv_supports(int64_t M, int64_t K)
+{
+    if (M < 1 || M > kSkinnyMaxM || K > kSkinnyMaxK || (M * K + 8) * 2 > kSkinnyMaxLdsBytes)
+        return false;
+    const int nit = chunk_iters(K);
+    return M <= max_rows(nit <= 4 ? 4 : nit <= 8 ? 8 : nit <= 12 ? 12 : 16);
+}
 
 hipError_t launch_gemv(const LinearProblem &pr, hipStream_t stream)
 {
@@ -175,10 +229,14 @@ hipError_t launch_gemv(const LinearProblem &pr, hipStream_t stream)
     gp.M = (int)pr.M;
     gp.N = (int)pr.N;
     gp.K = (int)pr.K;
-    const bool bias = pr.bias != nullptr;
-    if (pr.M <= 4)
-        return launch_bmax<4>(gp, pr.out_bf16, bias, pr.gelu, stream);
-    return launch_bmax<16>(gp, pr.out_bf16, bias, pr.gelu, stream);
+    const int nit = chunk_iters(gp.K);
+    if (nit <= 4)
+        return launch_rows<4>(gp, pr.out_bf16, pr.gelu, stream);
+    if (nit <= 8)
+        return launch_rows<8>(gp, pr.out_bf16, pr.gelu, stream);
+    if (nit <= 12)
+        return launch_rows<12>(gp, pr.out_bf16, pr.gelu, stream);
+    return launch_rows<16>(gp, pr.out_bf16, pr.gelu, stream);
 }
 
 }  // namespace tpl

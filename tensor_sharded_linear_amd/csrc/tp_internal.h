@@ -27,10 +27,14 @@ struct LinearProblem {
 // Tiled MFMA GEMM (M > kSkinnyMaxM).  Requires K % 64 == 0, N % 16 == 0.
 hipError_t launch_gemm(const LinearProblem &p, hipStream_t stream);
 
-// Weight-streaming kernel for M <= kSkinnyMaxM (skinny adaLN modulation shape).
-constexpr int64_t kSkinnyMaxM = 16;
-// Bytes of LDS the skinny kernel may use to stage the activation rows.
+// Weight-streaming kernel for skinny M (the adaLN modulation shape): each wave
+// holds whole weight rows of up to kSkinnyMaxK elements in registers, and the
+// M activation rows are staged in at most kSkinnyMaxLdsBytes of LDS.
+// gemv_supports() says whether (M, K) fits; other requests use the tiled kernel.
+constexpr int64_t kSkinnyMaxM = 8;
+constexpr int64_t kSkinnyMaxK = 8192;
 constexpr int64_t kSkinnyMaxLdsBytes = 96 * 1024;
+bool gemv_supports(int64_t M, int64_t K);
 hipError_t launch_gemv(const LinearProblem &p, hipStream_t stream);
 
 // Bit-exact strided copies: `rows` rows of `row_bytes` bytes each.
