@@ -83,7 +83,8 @@ typedef enum { TP_COMBINE_SUM = 0, TP_COMBINE_CONCAT = 1 } tp_combine;
  * fp32, one rounding to y_dtype (round to nearest even for bf16).
  * Small M (up to 8 rows, K <= 8192) uses a weight-streaming kernel (the skinny adaLN modulation shape),
  * larger M the tiled MFMA kernel; both obey the same contract.
- * Requires K % 64 == 0 and n_shard % 16 == 0 (TP_ERR_UNSUPPORTED otherwise).
+ * Requires K % 64 == 0 and n_shard % 16 == 0, and each operand view (rows x
+ * leading dimension) below 2 GiB (TP_ERR_UNSUPPORTED otherwise).
  */
 tp_status tp_linear_colwise(const void *x, int64_t ldx, const void *w_shard, int64_t ldw,
                             const void *bias, void *y, int64_t ldy, tp_dtype y_dtype,
@@ -104,7 +105,8 @@ tp_status tp_linear_colwise(const void *x, int64_t ldx, const void *w_shard, int
  *   partial [M, N]        fp32, row stride ldp (>= N, multiple of 4)
  *
  * Arithmetic: bf16 products, fp32 accumulation, fp32 store.
- * Requires k_shard % 64 == 0 and N % 16 == 0 (TP_ERR_UNSUPPORTED otherwise).
+ * Requires k_shard % 64 == 0 and N % 16 == 0, and each operand view (rows x
+ * leading dimension) below 2 GiB (TP_ERR_UNSUPPORTED otherwise).
  */
 tp_status tp_linear_rowwise(const void *x_shard, int64_t ldx, const void *w_shard, int64_t ldw,
                             float *partial, int64_t ldp, int64_t M, int64_t N, int64_t k_shard,

@@ -37,6 +37,7 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 int elem_size(tp_dtype d) { return d == TP_BF16 ? 2 : (d == TP_F32 ? 4 : 0); }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+constexpr int64_t kMaxOperandBytes = (int64_t)1 << 31;
 constexpr int kMaxBlocks = 16;
 
 // Common checks of the two compute entry points.  Returns TP_OK when the
@@ -64,6 +65,9 @@ tp_status check_linear(const char *fn, const void *x, int64_t ldx, const void *w
     if (ldy < N || (ldy * y_es) % 16 != 0)
         return fail(TP_ERR_INVALID_ARG, "%s: ldy=%lld must be >= N=%lld and a multiple of 16 bytes", fn,
                     (long long)ldy, (long long)N);
+    // The kernels address each operand by 32-bit byte offsets from its base.
+    if (((N - 1) * ldw + K) * 2 >= kMaxOperandBytes || (M > 0 && ((M - 1) * ldx + K) * 2 >= kMaxOperandBytes))
+        return fail(TP_ERR_UNSUPPORTED, "%s: an operand spans 2 GiB or more", fn);
     if (!w || !aligned(w, 16))
         return fail(TP_ERR_INVALID_ARG, "%s: weight pointer is null or not 16-byte aligned", fn);
     if (bias && !aligned(bias, 8))

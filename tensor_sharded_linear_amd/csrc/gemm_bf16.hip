@@ -9,24 +9,25 @@
 // block of W and X with an fp32 store and no bias (the partial sum).
 //
 // Design for gfx950:
-//  * 256 x 256 output tile per workgroup, K step 64, 256 threads = 4 waves in
-//    a 2 x 2 grid; each wave owns a 128 x 128 sub-tile held as 4 x 4 MFMA
-//    32x32 fp32 accumulators (v_mfma_f32_32x32x16_bf16), 256 accumulator
-//    registers per lane (the AGPR file), one wave per SIMD.  A 128 x 128 wave
-//    tile needs 64 flop per byte read from LDS, a third less LDS traffic per
-//    flop than 128 x 64.
+//  * 256 x 256 output tile per workgroup, K step 64, 512 threads = 8 waves in
+//    a 2 (M) x 4 (N) grid; each wave owns a 128 x 64 sub-tile held as 4 x 2
+//    MFMA 32x32 fp32 accumulators (128 accumulator registers per lane).  Two
+//    waves per SIMD, so one wave's LDS fragment reads overlap the other's
+//    MFMAs; one wave per SIMD left the LDS read port idle half the time.
 //  * Operands go HBM/L2 -> LDS by direct-to-LDS DMA (global_load_lds_dwordx4),
 //    no VGPR staging, double-buffered: 2 stages x (X tile + W tile) x 32 KiB =
 //    128 KiB of the 160 KiB LDS.
-//  * Fragments are double-buffered in registers at k16 granularity: while the
-//    16 MFMAs of one k16 step run, the 8 fragments of the next step are read
-//    from LDS.  The single barrier per k-tile sits before the last k16 step:
-//    after it the next k-tile has landed and every wave has finished reading
-//    the stage that the DMA for the k-tile after next then overwrites, so the
-//    DMA runs a whole k-tile ahead and no fragment read is exposed.
-//  * LDS tiles are 64-element (128-byte) rows; the 16-byte chunk c of row r is
-//    stored at position c ^ (r & 7), so the eight lanes that read one
-//    16-byte column of a fragment hit eight different bank groups.
+//  * Fragments are double-buffered in registers at k16 granularity: while
+//    the 8 MFMAs of one k16 step run, the 6 fragments of the next step are
+//    read from LDS.  The single barrier per k-tile sits before the last k16
+//    step: after it the next k-tile has landed and every wave has finished
+//    reading the stage that the DMA for the k-tile after next then
+//    overwrites, so the DMA runs a whole k-tile ahead and no fragment read is
+//    exposed.
+//  * LDS tiles are 64-element (128-byte) rows; the 16-byte chunk c of row r
+//    is stored at position c ^ ((r >> 1) & 7).  A fragment read covers 32
+//    rows of one chunk column; under this swizzle each group of lanes that
+//    the LDS serves together touches distinct banks.
 //  * The W fragment is the MFMA "A" operand and the X fragment the "B"
 //    operand, so each lane holds runs of four consecutive output columns of
 //    one row.  The epilogue applies bias / GELU / rounding, passes each
@@ -41,6 +42,7 @@
 //  * Ragged M and N: loads clamp the row index to the last valid row (the
 //    extra rows are computed and discarded), stores are masked.
 #include "tp_internal.h"
+#include <atomic>
 #include <type_traits>
 
 namespace tpl {
@@ -53,20 +55,27 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 #define TPL_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
-constexpr int BM = 256;
+// The tile height is a template parameter TM, the number of 32-row MFMA
+// blocks per wave: TM = 4 gives 256 x 256 tiles, TM = 3 gives 192 x 256
+// tiles (chosen when they fill the CUs better, see pick_tm).
 constexpr int BN = 256;
 constexpr int BK = 64;
 constexpr int kThreads = 512;     // 8 waves in a 2 (M) x 4 (N) grid
 constexpr int kWavesN = 4;
 constexpr int kWaves = kThreads / 64;
-constexpr int WM = 128;           // rows of the output owned by one wave
 constexpr int WN = 64;            // columns of the output owned by one wave
-constexpr int TM = WM / 32;       // 32-row MFMA tiles per wave
 constexpr int TN = WN / 32;       // 32-column MFMA tiles per wave
-constexpr int kDmaPerOperand = (BM * BK * 2) / (kThreads * 16);  // 16-byte DMAs per thread per tile
-constexpr int kTileElems = BM * BK;          // one operand tile (BM == BN)
-constexpr int kStageElems = 2 * kTileElems;  // X tile + W tile
-constexpr int kLdsElems = 2 * kStageElems;   // double buffered: 128 KiB
+constexpr int kDmaW = (BN * BK * 2) / (kThreads * 16);  // 16-byte DMAs per thread per W tile
+
+template <int TM>
+struct Tile {
+    static constexpr int WM = 32 * TM;   // rows of the output owned by one wave
+    static constexpr int BM = 2 * WM;    // rows of the output tile
+    static constexpr int kDmaX = (BM * BK * 2) / (kThreads * 16);  // 16-byte DMAs per thread per X tile
+    static constexpr int kXElems = BM * BK;
+    static constexpr int kStageElems = (BM + BN) * BK;  // X tile + W tile
+    static constexpr int kLdsElems = 2 * kStageElems;   // double buffered: 128 or 112 KiB
+};
 
 struct GemmParams {
     const uint16_t *x;
@@ -78,16 +87,21 @@ struct GemmParams {
     int tiles_m, tiles_n, group_m;
 };
 
-// Block index -> (tile row, tile column).  See the file header.
-__device__ __forceinline__ void tile_coords(int bid, const GemmParams &p, int &tm, int &tn)
+// Workgroups are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8).
+// Renumber [0, total) so that each XCD's blocks get a contiguous run.
+__device__ __forceinline__ int xcd_contiguous(int bid, int total)
 {
-    const int total = p.tiles_m * p.tiles_n;
     const int xcd = bid & 7;
     const int local = bid >> 3;
     const int per = (total + 7) >> 3;
     const int tall = total - (per - 1) * 8;  // XCDs that receive `per` blocks
-    const int lin = xcd < tall ? xcd * per + local
-                               : tall * per + (xcd - tall) * (per - 1) + local;
+    return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
+}
+
+// Linear tile index -> (tile row, tile column), grouped raster: group_m tile
+// rows at a time, column-major inside the group.
+__device__ __forceinline__ void tile_of(int lin, const GemmParams &p, int &tm, int &tn)
+{
     const int in_group = p.group_m * p.tiles_n;
     const int g = lin / in_group;
     const int first_m = g * p.group_m;
@@ -108,80 +122,101 @@ __device__ __forceinline__ float gelu_tanh(float v)
 }
 
 // One k16 step's operand fragments: per lane 8 bf16 of one row of each of
-// the wave's four 32-row X blocks and four 32-row W blocks.
+// the wave's TM 32-row X blocks and two 32-row W blocks.
+template <int TM>
 struct Frags {
     bf16x8 x[TM];
     bf16x8 w[TN];
 };
 
-template <bool OUT_BF16, bool HAS_BIAS, bool GELU>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_bf16_nt_kernel(GemmParams p)
+// Per-thread constants of the tile pipeline.
+struct Ctx {
+    int lane, wave, wave_m, wave_n;
+    int dma_row, dma_chunk;       // DMA: row within a 64-row group, logical chunk
+    int xrow_off, wrow_off;       // fragment row offsets inside an LDS tile
+    int swz, kh;                  // fragment swizzle and k-half
+};
+
+template <int TM>
+__device__ __forceinline__ Ctx make_ctx()
 {
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsElems];
+    Ctx c;
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int tm, tn;
-    tile_coords(blockIdx.x, p, tm, tn);
-    const int m0 = tm * BM;
-    const int n0 = tn * BN;
-
+    c.lane = tid & 63;
+    c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    c.wave_m = c.wave / kWavesN;
+    c.wave_n = c.wave % kWavesN;
     // DMA addressing.  Instruction j of wave w fills LDS chunks
-    // [(4j + w) * 64, +64) of a 256x64 tile: lane l lands at tile row
-    // 32j + 8w + l/8, stored position l%8, i.e. logical chunk (l%8) ^ (l/8).
-    const int dma_row = wave * 8 + (lane >> 3);
-    const int dma_chunk = (lane & 7) ^ ((((wave & 1) << 2) + (lane >> 4)) & 7);
-    const uint16_t *xsrc[kDmaPerOperand];
-    const uint16_t *wsrc[kDmaPerOperand];
-#pragma unroll
-    for (int j = 0; j < kDmaPerOperand; ++j) {
-        const int r = j * (8 * kWaves) + dma_row;
-        const int gm = min(m0 + r, p.M - 1);
-        const int gn = min(n0 + r, p.N - 1);
-        xsrc[j] = p.x + (int64_t)gm * p.ldx + dma_chunk * 8;
-        wsrc[j] = p.w + (int64_t)gn * p.ldw + dma_chunk * 8;
-    }
-
+    // [(8j + w) * 64, +64) of a 64-column tile: lane l lands at tile row
+    // R = 64j + 8w + l/8, stored position l%8, so it must fetch logical chunk
+    // (l%8) ^ ((R >> 1) & 7) = (l%8) ^ ((4 (w & 1) + l/16) & 7).
+    c.dma_row = c.wave * 8 + (c.lane >> 3);
+    c.dma_chunk = (c.lane & 7) ^ ((((c.wave & 1) << 2) + (c.lane >> 4)) & 7);
     // Fragment addressing: lane l reads row (l % 32) of a 32-row block,
-    // 16-byte k-chunk (2 s + l / 32) for k16 step s; the row's low 3 bits
-    // equal l % 8.
-    const int wave_m = wave / kWavesN;
-    const int wave_n = wave % kWavesN;
-    const int xrow_off = (wave_m * WM + (lane & 31)) * BK;
-    const int wrow_off = (wave_n * WN + (lane & 31)) * BK;
-    const int swz = (lane >> 1) & 7;
-    const int kh = lane >> 5;
-    f32x16 acc[TM][TN];
+    // 16-byte k-chunk (2 s + l / 32) for k16 step s, stored at position
+    // chunk ^ ((row >> 1) & 7) = chunk ^ ((l >> 1) & 7).
+    c.xrow_off = (c.wave_m * Tile<TM>::WM + (c.lane & 31)) * BK;
+    c.wrow_off = (c.wave_n * WN + (c.lane & 31)) * BK;
+    c.swz = (c.lane >> 1) & 7;
+    c.kh = c.lane >> 5;
+    return c;
+}
+
+// One 16-byte direct-to-LDS load per lane (global_load_lds_dwordx4): lane l
+// writes dst + 16 l bytes.  Kept out of templates: the host pass of a
+// template rejects the LDS address-space argument.
+__device__ __forceinline__ void dma16(const char *src, uint16_t *dst)
+{
+    __builtin_amdgcn_global_load_lds(src, TPL_LDS(dst), 16, 0, 0);
+}
+
+// acc += X[m0 .. m0+BM-1, k] . W[n0 .. n0+255, k]^T over k-tiles [kt0, kt1).
+// Starts with a barrier, so the LDS may still be in use by the caller's
+// previous tile when it is called.
+template <int TM>
+__device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, const Ctx &c, int m0, int n0,
+                                         int kt0, int kt1, f32x16 (&acc)[TM][TN])
+{
+    // Per-lane byte offsets (32-bit: operands are below 2 GiB) from
+    // wave-uniform bases, so the DMA uses the scalar-base addressing form.
+    const char *xbase = reinterpret_cast<const char *>(p.x) + (int64_t)kt0 * BK * 2;
+    const char *wbase = reinterpret_cast<const char *>(p.w) + (int64_t)kt0 * BK * 2;
+    typedef Tile<TM> L;
+    uint32_t xoff[L::kDmaX], woff[kDmaW];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < L::kDmaX; ++j) {
+        const int gm = min(m0 + j * (8 * kWaves) + c.dma_row, p.M - 1);
+        xoff[j] = (uint32_t)(((int64_t)gm * p.ldx + c.dma_chunk * 8) * 2);
+    }
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                acc[i][j][e] = 0.f;
+    for (int j = 0; j < kDmaW; ++j) {
+        const int gn = min(n0 + j * (8 * kWaves) + c.dma_row, p.N - 1);
+        woff[j] = (uint32_t)(((int64_t)gn * p.ldw + c.dma_chunk * 8) * 2);
+    }
     auto issue = [&](int stage, int k0) {
-        uint16_t *xs = lds + stage * kStageElems;
-        uint16_t *ws = xs + kTileElems;
+        uint16_t *xs = lds + stage * L::kStageElems;
+        uint16_t *ws = xs + L::kXElems;
+        const char *xb = xbase + k0 * 2;
+        const char *wb = wbase + k0 * 2;
 #pragma unroll
-        for (int j = 0; j < kDmaPerOperand; ++j)
-            __builtin_amdgcn_global_load_lds(xsrc[j] + k0, TPL_LDS(xs + (j * kWaves + wave) * 512), 16, 0, 0);
+        for (int j = 0; j < L::kDmaX; ++j)
+            dma16(xb + xoff[j], xs + (j * kWaves + c.wave) * 512);
 #pragma unroll
-        for (int j = 0; j < kDmaPerOperand; ++j)
-            __builtin_amdgcn_global_load_lds(wsrc[j] + k0, TPL_LDS(ws + (j * kWaves + wave) * 512), 16, 0, 0);
+        for (int j = 0; j < kDmaW; ++j)
+            dma16(wb + woff[j], ws + (j * kWaves + c.wave) * 512);
     };
-    auto read_frags = [&](int stage, int s, Frags &f) {
-        const uint16_t *xs = lds + stage * kStageElems;
-        const uint16_t *ws = xs + kTileElems;
-        const int cpos = ((s * 2 + kh) ^ swz) * 8;
+    auto read_frags = [&](int stage, int s, Frags<TM> &f) {
+        const uint16_t *xs = lds + stage * L::kStageElems;
+        const uint16_t *ws = xs + L::kXElems;
+        const int cpos = ((s * 2 + c.kh) ^ c.swz) * 8;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-            f.x[i] = *reinterpret_cast<const bf16x8 *>(xs + xrow_off + i * 32 * BK + cpos);
+            f.x[i] = *reinterpret_cast<const bf16x8 *>(xs + c.xrow_off + i * 32 * BK + cpos);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-            f.w[j] = *reinterpret_cast<const bf16x8 *>(ws + wrow_off + j * 32 * BK + cpos);
+            f.w[j] = *reinterpret_cast<const bf16x8 *>(ws + c.wrow_off + j * 32 * BK + cpos);
     };
-    auto mma = [&](const Frags &f) {
+    auto mma = [&](const Frags<TM> &f) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -189,9 +224,8 @@ void gemm_bf16_nt_kernel(GemmParams p)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[j], f.x[i], acc[i][j], 0, 0, 0);
     };
     // Pipeline: stage t % 2 holds k-tile t; steps s = 0..3 are its k16 slices.
-    // Each step issues the next step's 6 fragment reads interleaved with its
-    // first MFMAs (2 reads, 1 MFMA, three times, then 5 MFMAs), so the reads
-    // land while the step's remaining MFMAs run.
+    // TPL_STEP(read next, mma current) fixes the order of one step for the
+    // scheduler: MFMA, 2 reads, MFMA, 2 reads, MFMA, 2 reads, 5 MFMAs.
 #define TPL_STEP(RD, MM) do { RD; MM;                                    \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                \
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                \
@@ -201,8 +235,9 @@ void gemm_bf16_nt_kernel(GemmParams p)
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                \
         __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);                \
         __builtin_amdgcn_sched_barrier(0); } while (0)
-    const int T = p.K / BK;
-    Frags f0, f1;
+    const int T = kt1 - kt0;
+    Frags<TM> f0, f1;
+    __syncthreads();  // the LDS is free: the previous tile's reads are done
     issue(0, 0);
     __syncthreads();
     read_frags(0, 0, f0);
@@ -223,27 +258,32 @@ void gemm_bf16_nt_kernel(GemmParams p)
     TPL_STEP(read_frags((T - 1) & 1, 3, f1), mma(f0));
     mma(f1);
 #undef TPL_STEP
+}
 
-    // Epilogue through LDS.  Lane l holds Y[m][n..n+3] for m = row base +
-    // 32 i + l%32 and n = column base + 32 j + 8 q + 4 (l / 32).  For each of
-    // the wave's four 32-row slices the wave writes its 32 x 64 values (after
-    // bias / GELU / rounding) into a private LDS area with padded rows, then
-    // reads them back row-major and stores whole row segments: 4 rows x 256 B
-    // (fp32) or 8 rows x 128 B (bf16) per store instruction.
+// Epilogue through LDS.  Lane l holds Y[m][n..n+3] for m = row base +
+// 32 i + l%32 and n = column base + 32 j + 8 q + 4 (l / 32).  For each of
+// the wave's four 32-row slices the wave writes its 32 x 64 values (after
+// bias / GELU / rounding) into a private LDS area with padded rows, then
+// reads them back row-major and stores whole row segments: 4 rows x 256 B
+// (fp32) or 8 rows x 128 B (bf16) per store instruction.
+template <int TM, bool OUT_BF16, bool HAS_BIAS, bool GELU>
+__device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, const Ctx &c, int m0, int n0,
+                                         const f32x16 (&acc)[TM][TN])
+{
     __syncthreads();  // every wave is done reading the operand stages
     typedef typename std::conditional<OUT_BF16, __bf16, float>::type OutT;
     constexpr int kOutEs = sizeof(OutT);
     constexpr int kRowElems = WN + 16 / kOutEs;                 // 64 + one 16-byte pad
-    OutT *stage = reinterpret_cast<OutT *>(lds) + wave * 32 * kRowElems;
-    const int mrow = lane & 31;
-    const int ncol = 4 * (lane >> 5);
+    OutT *stage = reinterpret_cast<OutT *>(lds) + c.wave * 32 * kRowElems;
+    const int mrow = c.lane & 31;
+    const int ncol = 4 * (c.lane >> 5);
     f32x4 bj[TN][4];
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             bj[j][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int n = n0 + wave_n * WN + j * 32 + q * 8 + ncol;
+            const int n = n0 + c.wave_n * WN + j * 32 + q * 8 + ncol;
             if (HAS_BIAS && n < p.N) {
                 const bf16x4 bb = *reinterpret_cast<const bf16x4 *>(p.bias + n);
                 bj[j][q] = f32x4{(float)bb[0], (float)bb[1], (float)bb[2], (float)bb[3]};
@@ -252,8 +292,8 @@ void gemm_bf16_nt_kernel(GemmParams p)
     constexpr int kVec = 16 / kOutEs;              // elements per 16-byte vector
     constexpr int kVecPerRow = WN / kVec;          // 16 (fp32) or 8 (bf16)
     constexpr int kRowsPerPass = 64 / kVecPerRow;  // 4 (fp32) or 8 (bf16)
-    const int rd_row = lane / kVecPerRow;
-    const int rd_vec = lane % kVecPerRow;
+    const int rd_row = c.lane / kVecPerRow;
+    const int rd_vec = c.lane % kVecPerRow;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -275,8 +315,8 @@ void gemm_bf16_nt_kernel(GemmParams p)
                 else
                     *reinterpret_cast<f32x4 *>(dst) = v;
             }
-        const int mbase = m0 + wave_m * WM + i * 32;
-        const int ncol0 = n0 + wave_n * WN + rd_vec * kVec;
+        const int mbase = m0 + c.wave_m * Tile<TM>::WM + i * 32;
+        const int ncol0 = n0 + c.wave_n * WN + rd_vec * kVec;
 #pragma unroll
         for (int r = 0; r < 32; r += kRowsPerPass) {
             const int row = r + rd_row;
@@ -288,13 +328,77 @@ void gemm_bf16_nt_kernel(GemmParams p)
     }
 }
 
-template <bool OUT_BF16, bool HAS_BIAS, bool GELU>
-hipError_t launch_variant(const GemmParams &gp, hipStream_t stream)
+template <int TM>
+__device__ __forceinline__ void zero(f32x16 (&acc)[TM][TN])
 {
-    const dim3 grid(gp.tiles_m * gp.tiles_n);
-    const dim3 block(kThreads);
-    hipLaunchKernelGGL((gemm_bf16_nt_kernel<OUT_BF16, HAS_BIAS, GELU>), grid, block, 0, stream, gp);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[i][j][e] = 0.f;
+}
+
+// One BM x 256 output tile per workgroup.
+template <int TM, bool OUT_BF16, bool HAS_BIAS, bool GELU>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_bf16_nt_kernel(GemmParams p)
+{
+    constexpr int BM = Tile<TM>::BM;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[Tile<TM>::kLdsElems];
+    const Ctx c = make_ctx<TM>();
+    int tm, tn;
+    tile_of(xcd_contiguous(blockIdx.x, p.tiles_m * p.tiles_n), p, tm, tn);
+    f32x16 acc[TM][TN];
+    zero<TM>(acc);
+    mainloop<TM>(p, lds, c, tm * BM, tn * BN, 0, p.K / BK, acc);
+    epilogue<TM, OUT_BF16, HAS_BIAS, GELU>(p, lds, c, tm * BM, tn * BN, acc);
+}
+
+template <int TM, bool OUT_BF16, bool HAS_BIAS, bool GELU>
+hipError_t launch_tm(GemmParams gp, hipStream_t stream)
+{
+    gp.tiles_m = (gp.M + Tile<TM>::BM - 1) / Tile<TM>::BM;
+    gp.group_m = gp.tiles_m < 8 ? gp.tiles_m : 8;
+    hipLaunchKernelGGL((gemm_bf16_nt_kernel<TM, OUT_BF16, HAS_BIAS, GELU>), dim3(gp.tiles_m * gp.tiles_n),
+                       dim3(kThreads), 0, stream, gp);
     return hipGetLastError();
+}
+
+template <bool OUT_BF16, bool HAS_BIAS, bool GELU>
+hipError_t launch_variant(const GemmParams &gp, int tm, hipStream_t stream)
+{
+    return tm == 3 ? launch_tm<3, OUT_BF16, HAS_BIAS, GELU>(gp, stream)
+                   : launch_tm<4, OUT_BF16, HAS_BIAS, GELU>(gp, stream);
+}
+
+// Compute units of the current device (cached per device).
+int cu_count()
+{
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Tile height: the number of rounds of tiles over the CUs, times the tile's
+// share of a 256-row tile's work, with 5% added for the 192-row tile (5
+// fragment reads per 6 MFMAs instead of 6 per 8).
+int pick_tm(int M, int tiles_n, int cus)
+{
+    const int64_t t4 = (int64_t)((M + 255) / 256) * tiles_n;
+    const int64_t t3 = (int64_t)((M + 191) / 192) * tiles_n;
+    const double c4 = (double)((t4 + cus - 1) / cus);
+    const double c3 = (double)((t3 + cus - 1) / cus) * 0.75 * 1.05;
+    return c3 < c4 ? 3 : 4;
 }
 
 }  // namespace
@@ -312,20 +416,19 @@ hipError_t launch_gemm(const LinearProblem &pr, hipStream_t stream)
     gp.M = (int)pr.M;
     gp.N = (int)pr.N;
     gp.K = (int)pr.K;
-    gp.tiles_m = (int)((pr.M + BM - 1) / BM);
     gp.tiles_n = (int)((pr.N + BN - 1) / BN);
-    gp.group_m = gp.tiles_m < 8 ? gp.tiles_m : 8;
+    const int tm = pick_tm(gp.M, gp.tiles_n, cu_count());
     const bool bias = pr.bias != nullptr;
     const int sel = (pr.out_bf16 ? 4 : 0) | (bias ? 2 : 0) | (pr.gelu ? 1 : 0);
     switch (sel) {
-    case 0: return launch_variant<false, false, false>(gp, stream);
-    case 1: return launch_variant<false, false, true>(gp, stream);
-    case 2: return launch_variant<false, true, false>(gp, stream);
-    case 3: return launch_variant<false, true, true>(gp, stream);
-    case 4: return launch_variant<true, false, false>(gp, stream);
-    case 5: return launch_variant<true, false, true>(gp, stream);
-    case 6: return launch_variant<true, true, false>(gp, stream);
-    default: return launch_variant<true, true, true>(gp, stream);
+    case 0: return launch_variant<false, false, false>(gp, tm, stream);
+    case 1: return launch_variant<false, false, true>(gp, tm, stream);
+    case 2: return launch_variant<false, true, false>(gp, tm, stream);
+    case 3: return launch_variant<false, true, true>(gp, tm, stream);
+    case 4: return launch_variant<true, false, false>(gp, tm, stream);
+    case 5: return launch_variant<true, false, true>(gp, tm, stream);
+    case 6: return launch_variant<true, true, false>(gp, tm, stream);
+    default: return launch_variant<true, true, true>(gp, tm, stream);
     }
 }
 

@@ -82,6 +82,9 @@ def rowwise(**kw):
     (dict(y_dtype=7), B.TP_ERR_INVALID_ARG),
     (dict(act=3), B.TP_ERR_INVALID_ARG),
     (dict(K=(1 << 31)), B.TP_ERR_UNSUPPORTED),
+    # operand views of 2 GiB or more: the kernels use 32-bit byte offsets
+    (dict(M=1 << 20, ldx=1 << 10, ldw=1 << 10, K=1 << 10), B.TP_ERR_UNSUPPORTED),
+    (dict(N=1 << 20, ldy=1 << 20, ldx=1 << 10, ldw=1 << 10, K=1 << 10), B.TP_ERR_UNSUPPORTED),
 ])
 def test_colwise_validation(kw, status):
     assert colwise(**kw) == status
@@ -101,6 +104,7 @@ def test_colwise_and_rowwise_empty_is_noop():
     (dict(ldp=128), B.TP_ERR_INVALID_ARG),
     (dict(ldx=500), B.TP_ERR_INVALID_ARG),
     (dict(p=A3 + 8), B.TP_ERR_INVALID_ARG),
+    (dict(M=(1 << 20) + 1, ldx=1 << 10, ldw=1 << 10, K=1 << 10), B.TP_ERR_UNSUPPORTED),
 ])
 def test_rowwise_validation(kw, status):
     assert rowwise(**kw) == status

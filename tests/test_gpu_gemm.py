@@ -1,7 +1,11 @@
 """GPU parity of the colwise / rowwise GEMMs (tiled MFMA kernel and the skinny
 weight-streaming kernel) against the oracle, through the C ABI.
 
-Ragged shapes span several 256x256 tiles with partial tiles on both edges.
+Ragged shapes span several tiles with partial tiles on both edges.  The
+kernel picks its tile height per shape (192 or 256 rows, whichever needs less
+time in rounds of tiles over the CUs): on a 256-CU device every RAGGED and
+LARGE shape fits in one round and runs 192-row tiles, and TALL runs 256-row
+tiles (432 of them in two rounds, against 576 of 192 rows in three).
 Integer-valued inputs make every summation order exact, so there the GPU must
 equal the oracle bit for bit, which pins operand layout and indexing; random
 inputs are held to the stated tolerance and to the derived per-element bound.
@@ -147,3 +151,79 @@ def test_skinny_path_integer_exact(B):
     assert np.array_equal(dev_to_f64(y), oracle.colwise(c, w))
     p = tsl.tp_linear_rowwise(bits_to_dev(c), bits_to_dev(w))
     assert np.array_equal(dev_to_f64(p), oracle.linear(c, w))
+
+
+# Larger shapes: 1100 x 1040 x 2048 is ragged on both edges of a 5 x 5 tile
+# grid with 32 k-tiles; 4608 x 2304 x 3072 is a full-size rowwise shard.
+LARGE_SHAPES = [(1100, 1040, 2048), (4608, 2304, 3072)]
+
+
+@pytest.mark.parametrize("M,N,K", LARGE_SHAPES)
+def test_large_integer_inputs_exact(M, N, K):
+    rng = np.random.default_rng(M + K)
+    x = si.int_bf16(rng, (M, K), -4, 4)
+    w = si.int_bf16(rng, (N, K), -4, 4)
+    p = tsl.tp_linear_rowwise(bits_to_dev(x), bits_to_dev(w))
+    rows = np.unique(np.concatenate([np.arange(0, M, 97), [M - 1]]))
+    ref = oracle.linear(x, w, rows=rows)
+    assert np.array_equal(dev_to_f64(p)[rows], ref)
+    # every output element, against an exact integer product on the host
+    xi = torch.from_numpy(oracle.bf16_widen(x)).to(torch.float64)
+    wi = torch.from_numpy(oracle.bf16_widen(w)).to(torch.float64)
+    assert torch.equal(p.cpu().to(torch.float64), xi @ wi.T)
+
+
+@pytest.mark.parametrize("act", ["none", "gelu_tanh"])
+def test_large_random_vs_oracle(act):
+    M, N, K = LARGE_SHAPES[0]
+    rng = np.random.default_rng(17)
+    x = si.normal_bf16(rng, (M, K))
+    w = si.normal_bf16(rng, (N, K), 1 / np.sqrt(K))
+    b = si.normal_bf16(rng, (N,))
+    y = tsl.tp_linear_colwise(bits_to_dev(x), bits_to_dev(w), bits_to_dev(b), act=act)
+    rows = np.unique(np.concatenate([np.arange(0, M, 37), [M - 1, 255, 256, 511, 512]]))
+    a = oracle.ACT_GELU_TANH if act == "gelu_tanh" else oracle.ACT_NONE
+    ref = oracle.colwise(x, w, b, act=a, rows=rows)
+    check_close(dev_to_f64(y)[rows], ref, K, True, S=abs_dot(x[rows], w, b), what=f"large colwise {act}")
+
+
+def test_large_repeat_runs_and_output_dtypes_agree():
+    M, N, K = LARGE_SHAPES[1]
+    rng = np.random.default_rng(23)
+    x = bits_to_dev(si.normal_bf16(rng, (M, K)))
+    w = bits_to_dev(si.normal_bf16(rng, (N, K), 1 / np.sqrt(K)))
+    a = tsl.tp_linear_rowwise(x, w)
+    b = tsl.tp_linear_rowwise(x, w)
+    c = tsl.tp_linear_colwise(x, w, out_dtype=torch.float32)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(a.view(torch.int32), c.view(torch.int32))
+
+
+TALL = (4600, 6128, 128)
+
+
+def test_tall_integer_inputs_exact():
+    M, N, K = TALL
+    rng = np.random.default_rng(31)
+    x = si.int_bf16(rng, (M, K), -4, 4)
+    w = si.int_bf16(rng, (N, K), -4, 4)
+    b = si.int_bf16(rng, (N,), -8, 8)
+    y = tsl.tp_linear_colwise(bits_to_dev(x), bits_to_dev(w), bits_to_dev(b), out_dtype=torch.float32)
+    rows = np.unique(np.concatenate([np.arange(0, M, 211), [255, 256, M - 1]]))
+    assert np.array_equal(dev_to_f64(y)[rows], oracle.colwise(x, w, b, rows=rows))
+    xi = torch.from_numpy(oracle.bf16_widen(x)).to(torch.float64)
+    wi = torch.from_numpy(oracle.bf16_widen(w)).to(torch.float64)
+    bi = torch.from_numpy(oracle.bf16_widen(b)).to(torch.float64)
+    assert torch.equal(y.cpu().to(torch.float64), xi @ wi.T + bi)
+
+
+def test_tall_random_gelu_vs_oracle():
+    M, N, K = TALL
+    rng = np.random.default_rng(37)
+    x = si.normal_bf16(rng, (M, K))
+    w = si.normal_bf16(rng, (N, K), 1 / np.sqrt(K))
+    b = si.normal_bf16(rng, (N,))
+    y = tsl.tp_linear_colwise(bits_to_dev(x), bits_to_dev(w), bits_to_dev(b), act="gelu_tanh")
+    rows = np.unique(np.concatenate([np.arange(0, M, 149), [255, 256, 4351, 4352, M - 1]]))
+    ref = oracle.colwise(x, w, b, act=oracle.ACT_GELU_TANH, rows=rows)
+    check_close(dev_to_f64(y)[rows], ref, K, True, S=abs_dot(x[rows], w, b), what="tall colwise gelu")

@@ -5,7 +5,9 @@ Index work (slices, QKV split, CONCAT) and the SUM combine are checked bit for
 bit on whole tensors.  GEMM outputs are checked against the oracle on sampled
 rows (tile-edge rows plus seeded random rows, all columns, every rank), and on
 whole tensors through GPU-side invariants of the method: the colwise shards'
-outputs gather to the unsharded output, the rowwise partials sum to it.
+outputs gather to the unsharded output, the rowwise partials sum to it (to
+rounding: the GEMM may split a tile's k range across workgroups differently for
+the sharded and the unsharded shape).
 """
 import numpy as np
 import pytest
@@ -92,10 +94,11 @@ def test_attention_projections_p4():
     assert np.array_equal(total.cpu().numpy(), oracle.combine_sum([p.cpu().numpy() for p in parts]))
     check_close(dev_to_f64(_rows_of(total, rows)), oracle.linear(a["a"], a["w_o"], rows=rows), 3072,
                 False, S=abs_dot(a["a"][rows], a["w_o"]), what="attn out-proj sum vs unsharded")
-    # head-aligned shards gather back into the unsharded fused projection, bit for bit
+    # head-aligned shards gather back into the unsharded fused projection (the two runs may
+    # split k differently across workgroups, so they agree to rounding, not bit for bit)
     full = tsl.tp_linear_colwise(x, wqkv)
     cat = tsl.tp_partial_combine(qkv_out, "concat", blocks=[1, 1, 1])
-    assert torch.equal(cat.view(torch.int16), full.view(torch.int16))
+    check_close(dev_to_f64(cat), dev_to_f64(full), 3072, True, what="attn concat(qkv) vs unsharded")
 
 
 def test_mlp_p4():
@@ -175,12 +178,13 @@ def test_full_block(P):
     c_up = tsl.tp_partial_combine(up_out, "concat")
     assert np.array_equal(dev_to_bits(c_up), oracle.combine_concat([dev_to_bits(t) for t in up_out]))
 
-    # whole-tensor invariants against the unsharded layers on the GPU
+    # whole-tensor invariants against the unsharded layers on the GPU (agreement to rounding:
+    # sharded and unsharded runs may split k differently across workgroups)
     full_qkv = tsl.tp_linear_colwise(x, wqkv)
-    assert torch.equal(c_qkv.view(torch.int16), full_qkv.view(torch.int16))
+    check_close(dev_to_f64(c_qkv), dev_to_f64(full_qkv), hidden, True, what=f"P{P} concat(qkv) vs unsharded")
     del full_qkv
     full_up = tsl.tp_linear_colwise(x, w1, act="gelu_tanh")
-    assert torch.equal(c_up.view(torch.int16), full_up.view(torch.int16))
+    check_close(dev_to_f64(c_up), dev_to_f64(full_up), hidden, True, what=f"P{P} concat(up) vs unsharded")
     del full_up
     full_out = tsl.tp_linear_rowwise(A, wo)
     check_close(dev_to_f64(s_out), dev_to_f64(full_out), hidden, False, what=f"P{P} sum(out) vs unsharded")
