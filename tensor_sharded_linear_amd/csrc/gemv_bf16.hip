@@ -70,22 +70,24 @@ __device__ __forceinline__ float wave_sum(float v)
 }
 
 // NIT = 16-byte chunks per lane per row = ceil(K / 512); B = activation rows.
-// Lanes whose chunk index runs past the row re-read the row's last chunk and
-// pair it with a zero chunk kept after the activations in LDS, so neither the
-// loads nor the dot products branch per lane.  The epilogue options (bias,
+// The activations sit in LDS with a row pitch of K + 8: each row is followed by
+// a zero chunk.  Lanes whose chunk index runs past the row re-read the weight
+// row's last chunk and pair it with their activation row's zero chunk, so
+// neither the loads nor the dot products branch per lane.  The epilogue options (bias,
 // GELU, output dtype) are uniform runtime flags: they act once per row.
 template <int NIT, int B>
 __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(GemvParams p, int out_bf16, int gelu)
 {
-    extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [B][K], then 8 zeros
+    extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [B][K + 8], zeros in the last 8
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int nch = p.K >> 3;  // 16-byte chunks per row (K % 64 == 0)
     constexpr int UB = B >= 8 ? 1 : 8 / B;  // chunks per LDS batch (8 vectors)
 
+    const int pitch = p.K + 8;  // LDS row pitch of the activations
     auto wch = [&](int u) { return min(u * 64 + lane, nch - 1) * 8; };
-    auto xch = [&](int u) { return u * 64 + lane < nch ? (u * 64 + lane) * 8 : B * p.K; };
+    auto xch = [&](int u) { return u * 64 + lane < nch ? (u * 64 + lane) * 8 : p.K; };
 
     const int stride = gridDim.x * kWaves;
     int r0 = blockIdx.x * kWaves + wave;
@@ -108,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(GemvParams p, int o
             _Pragma("unroll") for (int u = 0; u < UB; ++u)                                   \
                 _Pragma("unroll") for (int b = 0; b < B; ++b)                                \
                     if (u0 + u < NIT)                                                        \
-                        xv_[u][b] = *reinterpret_cast<const bf16x8 *>(xs + b * p.K + xch(u0 + u)); \
+                        xv_[u][b] = *reinterpret_cast<const bf16x8 *>(xs + b * pitch + xch(u0 + u)); \
             _Pragma("unroll") for (int u = 0; u < UB; ++u)                                   \
                 _Pragma("unroll") for (int b = 0; b < B; ++b)                                \
                     if (u0 + u < NIT)                                                        \
@@ -134,11 +136,11 @@ __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(GemvParams p, int o
     for (int idx = tid; idx < B * nch; idx += kThreads) {
         const int bb = idx / nch;
         const int c = idx - bb * nch;
-        *reinterpret_cast<bf16x8 *>(xs + bb * p.K + c * 8) =
+        *reinterpret_cast<bf16x8 *>(xs + bb * pitch + c * 8) =
             *reinterpret_cast<const bf16x8 *>(p.x + (int64_t)bb * p.ldx + c * 8);
     }
-    if (tid == 0)
-        *reinterpret_cast<bf16x8 *>(xs + B * p.K) = bf16x8{};
+    if (tid < B)
+        *reinterpret_cast<bf16x8 *>(xs + tid * pitch + p.K) = bf16x8{};
     __syncthreads();
 
     // Two rows in flight per wave: A is reduced while B loads, and back.
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(GemvParams p, int o
 template <int NIT, int B>
 hipError_t launch_variant(const GemvParams &gp, bool out_bf16, bool gelu, hipStream_t stream)
 {
-    const size_t lds = ((size_t)B * gp.K + 8) * sizeof(uint16_t);
+    const size_t lds = (size_t)B * (gp.K + 8) * sizeof(uint16_t);
     auto kern = gemv_bf16_kernel<NIT, B>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -210,7 +212,7 @@ hipError_t launch_rows(const GemvParams &gp, bool out_bf16, bool gelu, hipStream
 
 bool gemv_supports(int64_t M, int64_t K)
 {
-    if (M < 1 || M > kSkinnyMaxM || K > kSkinnyMaxK || (M * K + 8) * 2 > kSkinnyMaxLdsBytes)
+    if (M < 1 || M > kSkinnyMaxM || K > kSkinnyMaxK || M * (K + 8) * 2 > kSkinnyMaxLdsBytes)
         return false;
     const int nit = chunk_iters(K);
     return M <= max_rows(nit <= 4 ? 4 : nit <= 8 ? 8 : nit <= 12 ? 12 : 16);

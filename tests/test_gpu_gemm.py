@@ -127,7 +127,7 @@ def test_repeat_runs_are_bitwise_identical():
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
-@pytest.mark.parametrize("B", [1, 2, 3, 4, 7, 16])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 6, 7, 8, 16])
 @pytest.mark.parametrize("act,bias", [("none", False), ("gelu_tanh", True)])
 def test_skinny_path_random(B, act, bias):
     rng = np.random.default_rng(B)
@@ -227,3 +227,23 @@ def test_tall_random_gelu_vs_oracle():
     rows = np.unique(np.concatenate([np.arange(0, M, 149), [255, 256, 4351, 4352, M - 1]]))
     ref = oracle.colwise(x, w, b, act=oracle.ACT_GELU_TANH, rows=rows)
     check_close(dev_to_f64(y)[rows], ref, K, True, S=abs_dot(x[rows], w, b), what="tall colwise gelu")
+
+
+@pytest.mark.parametrize("K", [512, 576, 1600, 4160])
+def test_skinny_path_reads_only_its_staged_rows(K):
+    """Lanes past the end of a row pair the weight's last chunk with their
+    activation row's zero chunk.  A tiled GEMM on 1e30-valued operands runs first
+    so that LDS holds huge stale values on every CU: a read outside the staged
+    rows would turn into inf or a wrong sum.  K is chosen so that every case has
+    lanes past the row end (K not a multiple of 512, or fewer chunks than the
+    kernel's chunk count)."""
+    big = torch.full((4096, 128), 1e30, dtype=torch.bfloat16, device="cuda")
+    tsl.tp_linear_colwise(big, big, out_dtype=torch.float32)
+    rng = np.random.default_rng(K)
+    N = 272
+    w = si.normal_bf16(rng, (N, K), 1 / np.sqrt(K))
+    wd = bits_to_dev(w)
+    for B in range(1, 9):
+        c = si.normal_bf16(rng, (B, K))
+        y = tsl.tp_linear_colwise(bits_to_dev(c), wd, out_dtype=torch.float32)
+        check_close(dev_to_f64(y), oracle.colwise(c, w), K, False, S=abs_dot(c, w), what=f"skinny K={K} B={B}")
