@@ -11,8 +11,12 @@ A step is one pass of the whole path over one batch of synthetic input:
     * layer-boundary combines: SUM of the out-proj partials (fp32) and of the
       FFN-down partials (bf16 out), CONCAT of the QKV outputs (packed [1,1,1])
       and of the FFN-up outputs;
-  adaLN modulation (6144 -> 36864, colwise P=4, 4 conditioning rows): shard
-  the weight for the 4 ranks, then each rank's skinny weight-streaming GEMV.
+  adaLN modulation (6144 -> 36864, P=4, 4 conditioning rows), twice:
+    * colwise: shard the weight for the 4 ranks, then each rank's skinny
+      weight-streaming GEMV;
+    * rowwise_split_input: shard the weight's input features for the 4 ranks,
+      each rank's skinny GEMV on its slice of the replicated input (fp32
+      partial), then the SUM of the 4 partials with the bias (bf16 out).
 
 Inputs are seeded synthetic bf16 tensors already resident in HBM when the timed
 region starts.  `value` is the step's sharded-linear TFLOP/s (all GEMM and GEMV
@@ -80,11 +84,11 @@ class Timer:
             c["flops"] += flops
             c["bytes"] += nbytes
             c["launches"] += 1
-            if cat == "gemm":
-                s = shapes.setdefault(key, dict(ms=0.0, flops=0.0, launches=0))
-                s["ms"] += ms
-                s["flops"] += flops
-                s["launches"] += 1
+            s = shapes.setdefault(f"{cat}: {key}", dict(ms=0.0, flops=0.0, bytes=0.0, launches=0))
+            s["ms"] += ms
+            s["flops"] += flops
+            s["bytes"] += nbytes
+            s["launches"] += 1
         return cats, shapes
 
 
@@ -154,6 +158,13 @@ def main():
         bufs[P] = b
     ada_w = [torch.empty(n_ada, hidden, dtype=torch.bfloat16, device=dev) for _ in range(P_ADA)]
     ada_y = [torch.empty(B_ADA, n_ada, dtype=torch.bfloat16, device=dev) for _ in range(P_ADA)]
+    # the same adaLN projection sharded rowwise_split_input: column blocks of W, fp32 partials, SUM
+    n_full_ada, k_ada = w_ada.shape[0], hidden // P_ADA
+    ada_ws = [torch.empty(n_full_ada, k_ada, dtype=torch.bfloat16, device=dev) for _ in range(P_ADA)]
+    ada_p = [torch.empty(B_ADA, n_full_ada, dtype=torch.float32, device=dev) for _ in range(P_ADA)]
+    ada_sum = torch.empty(B_ADA, n_full_ada, dtype=torch.bfloat16, device=dev)
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    b_ada = torch.randn(n_full_ada, generator=gen).to(torch.bfloat16).to(dev)
 
     T = Timer(torch)
     gemm_flops_step = 0.0
@@ -208,11 +219,23 @@ def main():
             T.run("gemv", f"adaLN B{B_ADA} {n_ada}x{hidden}", 2.0 * B_ADA * n_ada * hidden,
                   2.0 * n_ada * hidden + 2.0 * B_ADA * (hidden + n_ada),
                   lambda: tsl.tp_linear_colwise(c_ada, ada_w[r], out=ada_y[r]))
+        # adaLN modulation, rowwise_split_input: shard, each rank's partial from its input slice, SUM
+        for r in range(P_ADA):
+            T.run("slice", "w_ada split", 0, 2 * 2 * n_full_ada * k_ada,
+                  lambda: tsl.tp_plan_shard_slice(w_ada, None, "rowwise_split_input", P_ADA, r,
+                                                  w_out=ada_ws[r]))
+        for r in range(P_ADA):
+            T.run("gemv", f"adaLN split-input B{B_ADA} {n_full_ada}x{k_ada}", 2.0 * B_ADA * n_full_ada * k_ada,
+                  2.0 * n_full_ada * k_ada + 2.0 * B_ADA * k_ada + 4.0 * B_ADA * n_full_ada,
+                  lambda: tsl.tp_linear_rowwise_split_input(c_ada, ada_ws[r], P_ADA, r, out=ada_p[r]))
+        T.run("sum", f"adaLN P{P_ADA} bf16", 0, (P_ADA * 4.0 + 2.0) * B_ADA * n_full_ada + 2.0 * n_full_ada,
+              lambda: tsl.tp_partial_combine(ada_p, "sum", bias=b_ada, out=ada_sum))
 
     for P in tps:
         gemm_flops_step += P * 2.0 * M * hidden * (3 * H // P * hd + ffn // P) + \
             P * 2.0 * M * hidden * (hidden // P + ffn // P)
-    lin_flops_step = gemm_flops_step + P_ADA * 2.0 * B_ADA * n_ada * hidden
+    lin_flops_step = gemm_flops_step + P_ADA * 2.0 * B_ADA * n_ada * hidden \
+        + P_ADA * 2.0 * B_ADA * n_full_ada * k_ada
 
     for _ in range(args.warmup):
         step()
@@ -262,7 +285,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "DiT block linear set, every rank of tp 2/4/8 in turn (hidden 6144, 48 heads x 128, "
-                        "FFN 18432, 4608 tokens) + adaLN 6144->36864 colwise tp 4, 4 rows",
+                        "FFN 18432, 4608 tokens) + adaLN 6144->36864 at tp 4, 4 rows, colwise and "
+                        "rowwise_split_input",
             "tokens": M, "hidden": hidden, "ffn": ffn, "heads": H, "head_dim": hd,
             "tp_degrees": tps, "adaln_rows": B_ADA, "adaln_tp": P_ADA,
             "parallelism": "tp shares computed sequentially on 1 GPU",
@@ -282,9 +306,9 @@ def main():
     }
     if args.detail:
         for k, s in sorted(shapes.items()):
-            tf = s["flops"] / (s["ms"] * 1e-3) / 1e12
-            print(f"# {k:40s} launches={s['launches']:4d} avg_us={s['ms'] * 1e3 / s['launches']:9.1f} "
-                  f"TFLOP/s={tf:8.1f}", file=sys.stderr)
+            sec = s["ms"] * 1e-3
+            print(f"# {k:48s} launches={s['launches']:4d} avg_us={s['ms'] * 1e3 / s['launches']:9.1f} "
+                  f"TFLOP/s={s['flops'] / sec / 1e12:8.1f} GB/s={s['bytes'] / sec / 1e9:8.1f}", file=sys.stderr)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(result), flush=True)

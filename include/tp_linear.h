@@ -60,8 +60,11 @@ typedef enum { TP_BF16 = 0, TP_F32 = 1 } tp_dtype;
 typedef enum { TP_ACT_NONE = 0, TP_ACT_GELU_TANH = 1 } tp_act;
 
 /* [TP] "Colwise and rowwise": colwise shards output features (weight dim 0),
- * rowwise shards input features (weight dim 1). */
-typedef enum { TP_COLWISE = 0, TP_ROWWISE = 1 } tp_style;
+ * rowwise shards input features (weight dim 1).  rowwise_split_input also
+ * shards input features, for a standalone layer whose input is replicated on
+ * every rank: each rank cuts its own slice of that input.  Its weight shard is
+ * cut exactly like a rowwise one. */
+typedef enum { TP_COLWISE = 0, TP_ROWWISE = 1, TP_ROWWISE_SPLIT_INPUT = 2 } tp_style;
 
 /* [TP] opening definition: AllReduce (sum of partials) or AllGather (concat of
  * output slices) at the layer boundary, done here on one device. */
@@ -111,6 +114,32 @@ tp_status tp_linear_colwise(const void *x, int64_t ldx, const void *w_shard, int
 tp_status tp_linear_rowwise(const void *x_shard, int64_t ldx, const void *w_shard, int64_t ldw,
                             float *partial, int64_t ldp, int64_t M, int64_t N, int64_t k_shard,
                             hipStream_t stream);
+
+/*
+ * tp_linear_rowwise_split_input -- [TP] "Colwise and rowwise" (the
+ * rowwise_split_input style) and "What to leave out" (a large AdaLN
+ * modulation projection is sharded this way).  The input x_full [M, k_full]
+ * is the same on every rank.  Rank r of P takes its slice of the input
+ * features, x_r = x_full[:, r*k_full/P : (r+1)*k_full/P], and computes the
+ * partial sum P_r = x_r . W_r^T with its column block W_r [N, k_full/P] of the
+ * weight (tp_plan_shard_slice, TP_ROWWISE_SPLIT_INPUT).  Summing the P
+ * partials with the bias added once (tp_partial_combine, SUM) gives every
+ * output feature on every rank.
+ *
+ *   x_full  [M, k_full]    bf16, row stride ldx >= k_full
+ *   w_shard [N, k_full/P]  bf16, row stride ldw
+ *   partial [M, N]         fp32, row stride ldp (>= N, multiple of 4)
+ *
+ * Arithmetic as tp_linear_rowwise; small M (up to 8 rows, k_full/P <= 8192)
+ * uses the weight-streaming kernel.
+ * Errors (before any device work): TP_ERR_INVALID_ARG for tp_degree < 1 or
+ * rank outside [0, tp_degree); TP_ERR_NOT_DIVISIBLE if tp_degree does not
+ * divide k_full; then every check of tp_linear_rowwise on the slice.
+ */
+tp_status tp_linear_rowwise_split_input(const void *x_full, int64_t ldx, int64_t k_full,
+                                        const void *w_shard, int64_t ldw, float *partial,
+                                        int64_t ldp, int64_t M, int64_t N, int tp_degree,
+                                        int rank, hipStream_t stream);
 
 /*
  * tp_fused_qkv_split -- [TP] "Colwise and rowwise" (attention: colwise Q, K, V
@@ -174,9 +203,9 @@ tp_status tp_partial_combine(const void *const *parts, int num_parts, int64_t ld
  *
  *   TP_COLWISE: rows [r*O/P, (r+1)*O/P) -> w_shard [O/P, I]; the bias is cut
  *     the same way into b_shard [O/P].
- *   TP_ROWWISE: columns [r*I/P, (r+1)*I/P) -> w_shard [O, I/P]; a rowwise
- *     shard owns no bias slice (the bias is added once after the sum), so
- *     b_full and b_shard must be NULL.
+ *   TP_ROWWISE, TP_ROWWISE_SPLIT_INPUT: columns [r*I/P, (r+1)*I/P) ->
+ *     w_shard [O, I/P]; such a shard owns no bias slice (the bias is added
+ *     once after the sum), so b_full and b_shard must be NULL.
  *   blocks != NULL (host, num_blocks <= 16 proportional positive integers):
  *     packed sharding of the sharded dim, each block cut independently and the
  *     rank's pieces kept in block order.
@@ -189,7 +218,7 @@ tp_status tp_partial_combine(const void *const *parts, int num_parts, int64_t ld
  *   TP_ERR_NOT_DIVISIBLE if P does not divide the sharded dim, sum(blocks) does
  *   not divide it, or any single packed block is not divisible by P;
  *   TP_ERR_INVALID_ARG for P < 1, rank outside [0, P), bad style/dtype, a
- *   bias with TP_ROWWISE, or null pointers.
+ *   bias with a rowwise style, or null pointers.
  */
 tp_status tp_plan_shard_slice(const void *w_full, const void *b_full, void *w_shard,
                               void *b_shard, int64_t out_features, int64_t in_features,

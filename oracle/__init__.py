@@ -184,6 +184,16 @@ def rowwise(x_full, rank: int, tp_degree: int, w_shard, rows=None, threads=None)
                           m=m, col0=rank * k_loc)
 
 
+def rowwise_split_input(x_full, rank: int, tp_degree: int, w_shard, rows=None, threads=None) -> np.ndarray:
+    """[TP] "Colwise and rowwise" (the rowwise_split_input style): the input is the
+    same on every rank and each rank cuts its own slice of the input features, then
+    computes the rowwise partial ``x[:, r*K/P:(r+1)*K/P] . W_r^T`` (no bias); float64.
+    The P partials summed, plus the bias once, are the unsharded layer."""
+    x_full = _u16(x_full, "x")
+    check_plan("rowwise", tp_degree, rank, _u16(w_shard, "w").shape[0], x_full.shape[1])
+    return rowwise(x_full, rank, tp_degree, w_shard, rows, threads)
+
+
 # --------------------------------------------------------------------------------------
 # Slicing
 # --------------------------------------------------------------------------------------

@@ -17,13 +17,14 @@ from ._binding import (  # noqa: F401
     tp_last_error,
     tp_linear_colwise,
     tp_linear_rowwise,
+    tp_linear_rowwise_split_input,
     tp_partial_combine,
     tp_plan_shard_shape,
     tp_plan_shard_slice,
 )
 
 __all__ = [
-    "tp_linear_colwise", "tp_linear_rowwise", "tp_fused_qkv_split", "tp_partial_combine",
+    "tp_linear_colwise", "tp_linear_rowwise", "tp_linear_rowwise_split_input", "tp_fused_qkv_split", "tp_partial_combine",
     "tp_plan_shard_slice", "tp_plan_shard_shape", "tp_last_error", "load_library", "TPError",
     "TPValueError", "TPRuntimeError",
 ]

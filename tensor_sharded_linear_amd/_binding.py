@@ -29,6 +29,7 @@ TP_ACT_NONE = 0
 TP_ACT_GELU_TANH = 1
 TP_COLWISE = 0
 TP_ROWWISE = 1
+TP_ROWWISE_SPLIT_INPUT = 2
 TP_COMBINE_SUM = 0
 TP_COMBINE_CONCAT = 1
 
@@ -39,6 +40,7 @@ _I = ctypes.c_int
 SIGNATURES = {
     "tp_linear_colwise": (_I, [_P, _I64, _P, _I64, _P, _P, _I64, _I, _I, _I64, _I64, _I64, _P]),
     "tp_linear_rowwise": (_I, [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _P]),
+    "tp_linear_rowwise_split_input": (_I, [_P, _I64, _I64, _P, _I64, _P, _I64, _I64, _I64, _I, _I, _P]),
     "tp_fused_qkv_split": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P]),
     "tp_partial_combine": (_I, [ctypes.POINTER(_P), _I, _I64, _P, _I64, _I, _I, _I, _P,
                                 ctypes.POINTER(_I64), _I, _I64, _I64, _P]),
@@ -190,6 +192,31 @@ def tp_linear_rowwise(x_shard: torch.Tensor, w_shard: torch.Tensor, *,
     return out
 
 
+def tp_linear_rowwise_split_input(x_full: torch.Tensor, w_shard: torch.Tensor, tp_degree: int, rank: int, *,
+                                  out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """rowwise_split_input shard: fp32 partial ``out = x_full[:, slice_r] @ w_shard.T``.
+
+    ``x_full`` is the replicated input [M, K]; the library cuts rank ``rank``'s
+    slice of its K columns (K / tp_degree of them) itself.  ``w_shard`` is the
+    rank's column block [N, K / tp_degree] of the weight."""
+    lib = load_library()
+    x_full = _dev2d(x_full, "x_full", torch.bfloat16)
+    w_shard = _dev2d(w_shard, "w_shard", torch.bfloat16)
+    m, k_full = x_full.shape
+    n = w_shard.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x_full.device)
+    out = _dev2d(out, "out", torch.float32)
+    if tuple(out.shape) != (m, n):
+        raise ValueError(f"out must be [{m}, {n}]")
+    if tp_degree >= 1 and k_full % tp_degree == 0 and w_shard.shape[1] != k_full // tp_degree:
+        raise ValueError(f"w_shard is {tuple(w_shard.shape)} but the input slice has {k_full // tp_degree} columns")
+    _check(lib.tp_linear_rowwise_split_input(_ptr(x_full), _ld(x_full), k_full, _ptr(w_shard), _ld(w_shard),
+                                             _ptr(out), _ld(out), m, n, tp_degree, rank,
+                                             _stream(stream, x_full)))
+    return out
+
+
 def tp_fused_qkv_split(w_qkv: torch.Tensor, b_qkv: Optional[torch.Tensor], num_heads: int,
                        head_dim: int, tp_degree: int, rank: int, *,
                        w_out: Optional[torch.Tensor] = None, b_out: Optional[torch.Tensor] = None,
@@ -272,9 +299,9 @@ def tp_plan_shard_shape(out_features: int, in_features: int, style: str, tp_degr
 
 def _style(style: str) -> int:
     try:
-        return {"colwise": TP_COLWISE, "rowwise": TP_ROWWISE}[style]
+        return {"colwise": TP_COLWISE, "rowwise": TP_ROWWISE, "rowwise_split_input": TP_ROWWISE_SPLIT_INPUT}[style]
     except KeyError:
-        raise ValueError("style must be 'colwise' or 'rowwise'") from None
+        raise ValueError("style must be 'colwise', 'rowwise' or 'rowwise_split_input'") from None
 
 
 def _blocks(blocks):

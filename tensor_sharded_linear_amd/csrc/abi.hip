@@ -180,6 +180,47 @@ tp_status tp_linear_rowwise(const void *x_shard, int64_t ldx, const void *w_shar
     return run_linear(fn, p, stream);
 }
 
+tp_status tp_linear_rowwise_split_input(const void *x_full, int64_t ldx, int64_t k_full, const void *w_shard,
+                                        int64_t ldw, float *partial, int64_t ldp, int64_t M, int64_t N,
+                                        int tp_degree, int rank, hipStream_t stream)
+{
+    const char *fn = "tp_linear_rowwise_split_input";
+    g_msg[0] = 0;
+    if (tp_degree < 1)
+        return fail(TP_ERR_INVALID_ARG, "%s: tp_degree=%d must be >= 1", fn, tp_degree);
+    if (rank < 0 || rank >= tp_degree)
+        return fail(TP_ERR_INVALID_ARG, "%s: rank=%d outside [0, %d)", fn, rank, tp_degree);
+    if (k_full <= 0 || k_full > kMaxDim)
+        return fail(TP_ERR_INVALID_ARG, "%s: k_full=%lld must be in [1, 2^30]", fn, (long long)k_full);
+    if (k_full % tp_degree != 0)
+        return fail(TP_ERR_NOT_DIVISIBLE, "%s: tp_degree=%d does not divide k_full=%lld", fn, tp_degree,
+                    (long long)k_full);
+    const int64_t k_shard = k_full / tp_degree;
+    if (ldx < k_full)
+        return fail(TP_ERR_INVALID_ARG, "%s: ldx=%lld must be >= k_full=%lld", fn, (long long)ldx,
+                    (long long)k_full);
+    // The rank's slice of the replicated input: a column offset into x_full.
+    const void *x_r = x_full ? (const void *)((const uint16_t *)x_full + rank * k_shard) : nullptr;
+    bool noop;
+    tp_status s = check_linear(fn, x_r, ldx, w_shard, ldw, nullptr, partial, ldp, 4, M, N, k_shard, &noop);
+    if (s != TP_OK || noop)
+        return s;
+    tpl::LinearProblem p;
+    p.x = (const uint16_t *)x_r;
+    p.ldx = ldx;
+    p.w = (const uint16_t *)w_shard;
+    p.ldw = ldw;
+    p.bias = nullptr;
+    p.y = partial;
+    p.ldy = ldp;
+    p.M = M;
+    p.N = N;
+    p.K = k_shard;
+    p.out_bf16 = false;
+    p.gelu = false;
+    return run_linear(fn, p, stream);
+}
+
 tp_status tp_fused_qkv_split(const void *w_qkv, const void *b_qkv, void *w_shard, void *b_shard,
                              int64_t num_heads, int64_t head_dim, int64_t K, tp_dtype dtype,
                              int tp_degree, int rank, hipStream_t stream)
@@ -327,8 +368,8 @@ tp_status tp_plan_shard_slice(const void *w_full, const void *b_full, void *w_sh
     const int es = elem_size(dtype);
     if (!es)
         return fail(TP_ERR_INVALID_ARG, "%s: dtype must be TP_BF16 or TP_F32", fn);
-    if (style != TP_COLWISE && style != TP_ROWWISE)
-        return fail(TP_ERR_INVALID_ARG, "%s: style must be TP_COLWISE or TP_ROWWISE", fn);
+    if (style != TP_COLWISE && style != TP_ROWWISE && style != TP_ROWWISE_SPLIT_INPUT)
+        return fail(TP_ERR_INVALID_ARG, "%s: style must be TP_COLWISE, TP_ROWWISE or TP_ROWWISE_SPLIT_INPUT", fn);
     if (tp_degree < 1)
         return fail(TP_ERR_INVALID_ARG, "%s: tp_degree=%d must be >= 1", fn, tp_degree);
     if (rank < 0 || rank >= tp_degree)
@@ -359,7 +400,7 @@ tp_status tp_plan_shard_slice(const void *w_full, const void *b_full, void *w_sh
         return TP_OK;  // shape query
     if (!w_full || !aligned(w_full, (uintptr_t)es) || !aligned(w_shard, (uintptr_t)es))
         return fail(TP_ERR_INVALID_ARG, "%s: weight pointers must be non-null and element aligned", fn);
-    if (style == TP_ROWWISE && (b_full || b_shard))
+    if (style != TP_COLWISE && (b_full || b_shard))
         return fail(TP_ERR_INVALID_ARG,
                     "%s: a rowwise shard owns no bias slice (the bias is added once after the sum)", fn);
     if ((b_full == nullptr) != (b_shard == nullptr))

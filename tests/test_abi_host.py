@@ -31,8 +31,8 @@ def declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = tsl.load_library()
     syms = declared_symbols()
-    assert syms == {"tp_linear_colwise", "tp_linear_rowwise", "tp_fused_qkv_split",
-                    "tp_partial_combine", "tp_plan_shard_slice", "tp_last_error"}
+    assert syms == {"tp_linear_colwise", "tp_linear_rowwise", "tp_linear_rowwise_split_input",
+                    "tp_fused_qkv_split", "tp_partial_combine", "tp_plan_shard_slice", "tp_last_error"}
     for s in syms:
         assert hasattr(lib, s), s
     assert set(B.SIGNATURES) == syms
@@ -110,6 +110,28 @@ def test_rowwise_validation(kw, status):
     assert rowwise(**kw) == status
 
 
+def split_input(**kw):
+    a = dict(x=A, ldx=1024, k_full=1024, w=A2, ldw=256, p=A3, ldp=256, M=4, N=256, P=4, r=1, stream=None)
+    a.update(kw)
+    return _call("tp_linear_rowwise_split_input", *a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=0), B.TP_ERR_INVALID_ARG),
+    (dict(r=4), B.TP_ERR_INVALID_ARG),
+    (dict(r=-1), B.TP_ERR_INVALID_ARG),
+    (dict(k_full=1002, ldx=1008), B.TP_ERR_NOT_DIVISIBLE),  # 4 does not divide 1002
+    (dict(k_full=384, ldx=384), B.TP_ERR_UNSUPPORTED),      # slice of 96 columns: not a multiple of 64
+    (dict(ldx=1000), B.TP_ERR_INVALID_ARG),                  # ldx < k_full
+    (dict(ldw=100), B.TP_ERR_INVALID_ARG),                   # ldw < slice width
+    (dict(x=None), B.TP_ERR_INVALID_ARG),
+    (dict(p=A3 + 4), B.TP_ERR_INVALID_ARG),
+])
+def test_split_input_validation(kw, status):
+    assert split_input(**kw) == status
+    assert tsl.tp_last_error().startswith("tp_linear_rowwise_split_input")
+
+
 def qkv(**kw):
     a = dict(w=A, b=None, ws=A2, bs=None, H=24, hd=128, K=3072, dtype=B.TP_BF16, P=4, r=0,
              stream=None)
@@ -147,6 +169,13 @@ def shape_query(o, i, style, P, r, blocks=None):
     return tsl.tp_plan_shard_shape(o, i, style, P, r, blocks)
 
 
+def test_split_input_shard_shape_is_the_rowwise_shape():
+    """[TP]: a rowwise_split_input weight is cut along the input features, like rowwise."""
+    for o, i, P in [(36864, 6144, 4), (256, 1024, 2), (8, 12, 3)]:
+        assert shape_query(o, i, "rowwise_split_input", P, P - 1) == shape_query(o, i, "rowwise", P, P - 1) \
+            == (o, i // P)
+
+
 @pytest.mark.parametrize("o,i,style,P,blocks", [
     (1024, 256, "colwise", 2, None), (256, 1024, "rowwise", 2, None),
     (9216, 3072, "colwise", 4, [1, 1, 1]), (18432, 6144, "colwise", 8, [1, 1, 1]),
@@ -176,6 +205,8 @@ def test_shard_shape_query_agrees_with_oracle_plan_rules(o, i, style, P, blocks)
     (dict(o=0), B.TP_ERR_INVALID_ARG), (dict(blocks=[0, 1]), B.TP_ERR_INVALID_ARG),
     (dict(blocks=[1] * 17), B.TP_ERR_INVALID_ARG),
     (dict(style=B.TP_ROWWISE, b=A3, bs=A3 + 64), B.TP_ERR_INVALID_ARG),
+    (dict(style=B.TP_ROWWISE_SPLIT_INPUT, b=A3, bs=A3 + 64), B.TP_ERR_INVALID_ARG),
+    (dict(style=B.TP_ROWWISE_SPLIT_INPUT, i=33), B.TP_ERR_NOT_DIVISIBLE),
     (dict(b=A3), B.TP_ERR_INVALID_ARG), (dict(w=None), B.TP_ERR_INVALID_ARG),
 ])
 def test_shard_slice_validation(args, status):

@@ -5,9 +5,9 @@ Index work (slices, QKV split, CONCAT) and the SUM combine are checked bit for
 bit on whole tensors.  GEMM outputs are checked against the oracle on sampled
 rows (tile-edge rows plus seeded random rows, all columns, every rank), and on
 whole tensors through GPU-side invariants of the method: the colwise shards'
-outputs gather to the unsharded output, the rowwise partials sum to it (to
-rounding: the GEMM may split a tile's k range across workgroups differently for
-the sharded and the unsharded shape).
+outputs gather to the unsharded output, the rowwise partials sum to it (held
+to rounding, not bit for bit: the method does not promise that a sharded and an
+unsharded shape accumulate in the same order).
 """
 import numpy as np
 import pytest

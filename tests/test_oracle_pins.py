@@ -295,6 +295,43 @@ def test_rowwise_strided_input_matches_copied_slice():
         assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("P", [1, 2, 4])
+def test_rowwise_split_input_brute_force_and_allreduce(P):
+    """[TP] rowwise_split_input: rank r computes from columns [r*K/P, (r+1)*K/P) of the
+    replicated input; adding the bias once to the sum of the P partials is the
+    unsharded layer (a skinny AdaLN-like shape: 3 conditioning rows)."""
+    rng = np.random.default_rng(50 + P)
+    b_rows, n, k = 3, 10, 32
+    x = si.normal_bf16(rng, (b_rows, k))
+    w = si.normal_bf16(rng, (n, k))
+    xf = [[Fraction(float(v)) for v in row] for row in oracle.bf16_widen(x)]
+    wf = [[Fraction(float(v)) for v in row] for row in oracle.bf16_widen(w)]
+    kl = k // P
+    parts = []
+    for r in range(P):
+        got = oracle.rowwise_split_input(x, r, P, oracle.shard_rowwise(w, P, r))
+        for i in range(b_rows):
+            for o in range(n):
+                terms = [xf[i][r * kl + j] * wf[o][r * kl + j] for j in range(kl)]
+                exact = sum(terms)  # bf16 products are exact rationals
+                assert abs(Fraction(got[i, o]) - exact) <= sum(abs(t) for t in terms) * Fraction(_gamma(kl))
+        parts.append(got)
+    b = si.normal_bf16(rng, (n,))
+    tot = np.sum(parts, axis=0) + oracle.bf16_widen(b)[None, :]
+    full = oracle.linear(x, w, b)
+    bound = 2 * _gamma(k + P + 1) * (np.abs(oracle.bf16_widen(x)) @ np.abs(oracle.bf16_widen(w)).T
+                                     + np.abs(oracle.bf16_widen(b))[None, :])
+    assert np.all(np.abs(tot - full) <= bound)
+
+
+def test_rowwise_split_input_checks_the_plan():
+    x = np.zeros((2, 30), np.uint16)
+    with pytest.raises(oracle.PlanError):
+        oracle.rowwise_split_input(x, 0, 4, np.zeros((3, 7), np.uint16))   # 4 does not divide 30
+    with pytest.raises(oracle.PlanError):
+        oracle.rowwise_split_input(x, 3, 3, np.zeros((3, 10), np.uint16))  # rank out of range
+
+
 # --------------------------------------------------------------------------------------
 # slicing
 # --------------------------------------------------------------------------------------
