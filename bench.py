@@ -52,7 +52,62 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--detail", action="store_true", help="also print a per-shape GEMM table to stderr")
+    ap.add_argument("--probe", metavar="OUT_JSON",
+                    help="untimed: two steps, then a calibration copy of known size, for rocprofv3 --pmc "
+                         "FETCH_SIZE / WRITE_SIZE runs; writes the step's algorithmic GEMM bytes to OUT_JSON")
+    ap.add_argument("--traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PROBE_JSON"),
+                    help="no GPU: reduce the two counter runs of --probe to " + os.path.relpath(TRAFFIC_FILE, ROOT))
     return ap.parse_args()
+
+
+CAL_ROWS, CAL_COLS = 8192, 8192   # calibration copy: a 128 MiB bf16 weight, copied whole (colwise, P = 1)
+
+
+def _counter_rows(d):
+    """Per-dispatch counter values of a rocprofv3 --pmc CSV run: [(dispatch, kernel, value)]."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one counter_collection.csv under {d}, found {files}")
+    out = {}
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            key = int(r["Dispatch_Id"])
+            out[key] = (r["Kernel_Name"], out.get(key, (None, 0.0))[1] + float(r["Counter_Value"]))
+    return [(k, n, v) for k, (n, v) in sorted(out.items())]
+
+
+def reduce_traffic(fetch_dir, write_dir, probe_json):
+    """HBM bytes per GEMM launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+    scaled by what the same counter reads for the calibration copy (CAL bytes read and
+    written), averaged over the GEMM launches of the probe's last step."""
+    with open(probe_json) as f:
+        probe = json.load(f)
+    res = {}
+    for name, d in (("fetch", fetch_dir), ("write", write_dir)):
+        rows = _counter_rows(d)
+        gemm = [v for _, n, v in rows if "gemm_bf16_nt_kernel" in n]
+        cal = [v for _, n, v in rows if "copy_segments_kernel" in n][-1]
+        last = gemm[-probe["gemm_launches_per_step"]:]
+        factor = probe["cal_bytes"] / (cal * 1024.0)
+        res[name] = dict(kib_per_launch=sum(last) / len(last), calibration_kib=cal, factor=factor,
+                         bytes_per_launch=sum(last) / len(last) * 1024.0 * factor)
+    total = res["fetch"]["bytes_per_launch"] + res["write"]["bytes_per_launch"]
+    out = {
+        "kernel": "gemm_bf16_nt_kernel",
+        "source_sha": file_sha(GEMM_SRC),
+        "bytes_per_launch": round(total),
+        "algorithmic_bytes_per_launch": round(probe["alg_bytes_per_launch"]),
+        "ratio_to_algorithmic": round(total / probe["alg_bytes_per_launch"], 4),
+        "fetch": res["fetch"], "write": res["write"],
+        "calibration": f"copy_segments_kernel copying a {CAL_ROWS}x{CAL_COLS} bf16 weight: "
+                       f"{probe['cal_bytes']} bytes read and the same written",
+        "launches_averaged": probe["gemm_launches_per_step"],
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 class Timer:
@@ -99,6 +154,9 @@ def file_sha(path):
 
 def main():
     args = parse()
+    if args.traffic:
+        reduce_traffic(*args.traffic)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU's share on one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) "
@@ -236,6 +294,23 @@ def main():
             P * 2.0 * M * hidden * (hidden // P + ffn // P)
     lin_flops_step = gemm_flops_step + P_ADA * 2.0 * B_ADA * n_ada * hidden \
         + P_ADA * 2.0 * B_ADA * n_full_ada * k_ada
+
+    if args.probe:
+        step()
+        torch.cuda.synchronize()
+        T.on = True
+        step()
+        torch.cuda.synchronize()
+        T.on = False
+        g = [r for r in T.rec if r[0] == "gemm"]
+        cal = torch.empty(CAL_ROWS, CAL_COLS, dtype=torch.bfloat16, device=dev)
+        tsl.tp_plan_shard_slice(cal, None, "colwise", 1, 0)
+        torch.cuda.synchronize()
+        with open(args.probe, "w") as f:
+            json.dump(dict(gemm_launches_per_step=len(g), alg_bytes_per_launch=sum(r[3] for r in g) / len(g),
+                           cal_bytes=2 * CAL_ROWS * CAL_COLS), f)
+        print(f"probe: {len(g)} GEMM launches per step", flush=True)
+        return
 
     for _ in range(args.warmup):
         step()
