@@ -11,6 +11,9 @@ A step is one pass of the whole path over one batch of synthetic input:
     * layer-boundary combines: SUM of the out-proj partials (fp32) and of the
       FFN-down partials (bf16 out), CONCAT of the QKV outputs (packed [1,1,1])
       and of the FFN-up outputs;
+  FLUX.2-style fused FFN gate/up projection (6144 -> 2 x 18432, packed with
+  blocks [1, 1], P=4): packed slices for the 4 ranks, then each rank's GEMM
+  with the fused SwiGLU epilogue (bf16 [4608, 4608] out);
   adaLN modulation (6144 -> 36864, P=4, 4 conditioning rows), twice:
     * colwise: shard the weight for the 4 ranks, then each rank's skinny
       weight-streaming GEMV;
@@ -188,7 +191,9 @@ def main():
     wqkv, wo = up(fb.arrays["w_qkv"]), up(fb.arrays["w_o"])
     w1, w2 = up(fb.arrays["w1"]), up(fb.arrays["w2"])
     c_ada, w_ada = up(ada.arrays["c"]), up(ada.arrays["w_ada"])
-    del fb, ada
+    gu = si.workload("swiglu_ffn")
+    x_gu, w_gu, b_gu = up(gu.arrays["x"]), up(gu.arrays["w_gu"]), up(gu.arrays["b_gu"])
+    del fb, ada, gu
     si.workload.cache_clear()
     print(f"# inputs generated and uploaded in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
 
@@ -221,6 +226,12 @@ def main():
     ada_ws = [torch.empty(n_full_ada, k_ada, dtype=torch.bfloat16, device=dev) for _ in range(P_ADA)]
     ada_p = [torch.empty(B_ADA, n_full_ada, dtype=torch.float32, device=dev) for _ in range(P_ADA)]
     ada_sum = torch.empty(B_ADA, n_full_ada, dtype=torch.bfloat16, device=dev)
+    # FLUX.2-style fused gate/up projection, blocks [1, 1], SwiGLU epilogue, tp 4
+    P_GU = 4
+    n_gu = ffn // P_GU
+    gu_w = [torch.empty(2 * n_gu, hidden, dtype=torch.bfloat16, device=dev) for _ in range(P_GU)]
+    gu_b = [torch.empty(2 * n_gu, dtype=torch.bfloat16, device=dev) for _ in range(P_GU)]
+    gu_y = [torch.empty(M, n_gu, dtype=torch.bfloat16, device=dev) for _ in range(P_GU)]
     gen = torch.Generator(device="cpu").manual_seed(5)
     b_ada = torch.randn(n_full_ada, generator=gen).to(torch.bfloat16).to(dev)
 
@@ -269,6 +280,15 @@ def main():
                   lambda: tsl.tp_partial_combine(b["q"], "concat", blocks=[1, 1, 1], out=b["q_cat"]))
             T.run("concat", "up", 0, 2 * 2.0 * M * ffn,
                   lambda: tsl.tp_partial_combine(b["h"], "concat", out=b["h_cat"]))
+        # fused gate/up projection with SwiGLU: packed [1, 1] slices, then each rank's GEMM
+        for r in range(P_GU):
+            T.run("slice", "w_gu [1,1]", 0, 2 * 2 * 2 * n_gu * hidden,
+                  lambda: tsl.tp_plan_shard_slice(w_gu, b_gu, "colwise", P_GU, r, blocks=[1, 1],
+                                                  w_out=gu_w[r], b_out=gu_b[r]))
+        for r in range(P_GU):
+            f, by = gemm_cost(M, 2 * n_gu, hidden, 0)
+            T.run("gemm", f"colwise+swiglu {M}x{2 * n_gu}x{hidden}", f, by + 2.0 * M * n_gu,
+                  lambda: tsl.tp_linear_colwise(x_gu, gu_w[r], gu_b[r], act="swiglu", out=gu_y[r]))
         # adaLN modulation: shard for 4 ranks, then each rank's skinny GEMV
         for r in range(P_ADA):
             T.run("slice", "w_ada", 0, 2 * 2 * n_ada * hidden,
@@ -292,6 +312,7 @@ def main():
     for P in tps:
         gemm_flops_step += P * 2.0 * M * hidden * (3 * H // P * hd + ffn // P) + \
             P * 2.0 * M * hidden * (hidden // P + ffn // P)
+    gemm_flops_step += P_GU * 2.0 * M * 2 * n_gu * hidden
     lin_flops_step = gemm_flops_step + P_ADA * 2.0 * B_ADA * n_ada * hidden \
         + P_ADA * 2.0 * B_ADA * n_full_ada * k_ada
 
@@ -360,8 +381,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "DiT block linear set, every rank of tp 2/4/8 in turn (hidden 6144, 48 heads x 128, "
-                        "FFN 18432, 4608 tokens) + adaLN 6144->36864 at tp 4, 4 rows, colwise and "
-                        "rowwise_split_input",
+                        "FFN 18432, 4608 tokens) + FLUX.2-style fused gate/up 6144->2x18432 with SwiGLU at tp 4 "
+                        "+ adaLN 6144->36864 at tp 4, 4 rows, colwise and rowwise_split_input",
             "tokens": M, "hidden": hidden, "ffn": ffn, "heads": H, "head_dim": hd,
             "tp_degrees": tps, "adaln_rows": B_ADA, "adaln_tp": P_ADA,
             "parallelism": "tp shares computed sequentially on 1 GPU",

@@ -56,8 +56,12 @@ typedef enum {
 
 typedef enum { TP_BF16 = 0, TP_F32 = 1 } tp_dtype;
 
-/* GELU with the tanh approximation: g(v) = v/2 (1 + tanh(sqrt(2/pi)(v + 0.044715 v^3))). */
-typedef enum { TP_ACT_NONE = 0, TP_ACT_GELU_TANH = 1 } tp_act;
+/* GELU with the tanh approximation: g(v) = v/2 (1 + tanh(sqrt(2/pi)(v + 0.044715 v^3))).
+ * SwiGLU of a packed [gate; up] projection ([TP] "Fused projections": blocks
+ * {1, 1} for a SwiGLU gate and up projection of equal halves): the weight
+ * holds 2 n rows, gate then up, and the n outputs are
+ * silu(x . gate^T + b_gate) * (x . up^T + b_up), silu(v) = v / (1 + e^-v). */
+typedef enum { TP_ACT_NONE = 0, TP_ACT_GELU_TANH = 1, TP_ACT_SWIGLU = 2 } tp_act;
 
 /* [TP] "Colwise and rowwise": colwise shards output features (weight dim 0),
  * rowwise shards input features (weight dim 1).  rowwise_split_input also
@@ -80,12 +84,17 @@ typedef enum { TP_COMBINE_SUM = 0, TP_COMBINE_CONCAT = 1 } tp_combine;
  *   w_shard [n_shard, K]  bf16, row stride ldw (>= K)
  *   bias    [n_shard]     bf16, or NULL (no bias); 8-byte alignment suffices
  *   y       [M, n_shard]  y_dtype (TP_BF16 or TP_F32), row stride ldy (>= n_shard)
- *   act     TP_ACT_NONE or TP_ACT_GELU_TANH, applied after the bias
+ *   act     TP_ACT_NONE or TP_ACT_GELU_TANH, applied after the bias; or
+ *           TP_ACT_SWIGLU: w_shard then holds 2 n_shard rows, the rank's gate
+ *           rows followed by its up rows (what tp_plan_shard_slice cuts from a
+ *           [gate; up] weight with blocks {1, 1}), bias likewise 2 n_shard
+ *           entries [b_gate; b_up] or NULL, and
+ *           y = silu(x . gate^T + b_gate) * (x . up^T + b_up)
  *
  * Arithmetic: bf16 products, fp32 accumulation (MFMA), bias and activation in
  * fp32, one rounding to y_dtype (round to nearest even for bf16).
  * Small M (up to 8 rows, K <= 8192) uses a weight-streaming kernel (the skinny adaLN modulation shape),
- * larger M the tiled MFMA kernel; both obey the same contract.
+ * larger M, and SwiGLU at any M, the tiled MFMA kernel; both obey the same contract.
  * Requires K % 64 == 0 and n_shard % 16 == 0, and each operand view (rows x
  * leading dimension) below 2 GiB (TP_ERR_UNSUPPORTED otherwise).
  */

@@ -184,6 +184,26 @@ def rowwise(x_full, rank: int, tp_degree: int, w_shard, rows=None, threads=None)
                           m=m, col0=rank * k_loc)
 
 
+def colwise_swiglu(x, w_shard, b_shard=None, rows=None, threads=None) -> np.ndarray:
+    """[TP] "Fused projections": a SwiGLU gate and up projection packed with blocks
+    [1, 1]; a rank's shard holds its gate rows then its up rows (2 n rows).  Output
+    ``silu(g) * u`` with ``g = x . gate^T + b_gate`` and ``u = x . up^T + b_up`` in
+    float64, ``silu(v) = v / (1 + e^-v)`` (the Swish gate of SwiGLU); float64 before
+    the output rounding."""
+    w = _u16(w_shard, "w")
+    if w.shape[0] % 2:
+        raise ValueError("a SwiGLU shard has an even number of rows [gate; up]")
+    n = w.shape[0] // 2
+    bg = bu = None
+    if b_shard is not None:
+        b = _u16(b_shard, "b")
+        bg, bu = b[:n], b[n:]
+    g = linear(x, np.ascontiguousarray(w[:n]), bg, ACT_NONE, rows, threads)
+    u = linear(x, np.ascontiguousarray(w[n:]), bu, ACT_NONE, rows, threads)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
+
+
 def rowwise_split_input(x_full, rank: int, tp_degree: int, w_shard, rows=None, threads=None) -> np.ndarray:
     """[TP] "Colwise and rowwise" (the rowwise_split_input style): the input is the
     same on every rank and each rank cuts its own slice of the input features, then

@@ -132,12 +132,23 @@ def adaln() -> Workload:
                     dict(hidden=6144, out=36864))
 
 
+def swiglu_ffn() -> Workload:
+    """FLUX.2-style fused gate/up projection of the FFN, packed with blocks [1, 1]:
+    hidden 6144 -> 2 x 18432 (gate then up), 4608 tokens, P=4.  Seed 5.
+    x; W_gu[36864,6144]; b_gu[36864]."""
+    spec = [("x", (4608, 6144), 1.0), ("w_gu", (36864, 6144), 1.0 / np.sqrt(6144.0)),
+            ("b_gu", (36864,), 1.0)]
+    return Workload("swiglu_ffn_h6144_f18432_p4", 5, (4,), _draw(5, spec),
+                    dict(M=4608, hidden=6144, ffn=18432))
+
+
 WORKLOADS = {
     "tiny_mlp": tiny_mlp,
     "attention_proj": attention_proj,
     "mlp_large": mlp_large,
     "full_block": full_block,
     "adaln": adaln,
+    "swiglu_ffn": swiglu_ffn,
 }
 
 

@@ -27,6 +27,7 @@ TP_BF16 = 0
 TP_F32 = 1
 TP_ACT_NONE = 0
 TP_ACT_GELU_TANH = 1
+TP_ACT_SWIGLU = 2
 TP_COLWISE = 0
 TP_ROWWISE = 1
 TP_ROWWISE_SPLIT_INPUT = 2
@@ -152,21 +153,30 @@ def _vec(t: Optional[torch.Tensor], name: str, n: int) -> Optional[torch.Tensor]
 def tp_linear_colwise(x: torch.Tensor, w_shard: torch.Tensor, bias: Optional[torch.Tensor] = None,
                       *, act: str = "none", out: Optional[torch.Tensor] = None,
                       out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
-    """Colwise shard: ``out = act(x @ w_shard.T + bias)`` (bf16 in, fp32 accumulate)."""
+    """Colwise shard: ``out = act(x @ w_shard.T + bias)`` (bf16 in, fp32 accumulate).
+
+    ``act="swiglu"``: ``w_shard`` is a packed [gate; up] shard of 2 n rows (and ``bias``
+    2 n entries); ``out`` [M, n] = silu(x @ gate.T + b_gate) * (x @ up.T + b_up)."""
     lib = load_library()
     x = _dev2d(x, "x", torch.bfloat16)
     w_shard = _dev2d(w_shard, "w_shard", torch.bfloat16)
     m, k = x.shape
-    n = w_shard.shape[0]
+    try:
+        a = {"none": TP_ACT_NONE, "gelu_tanh": TP_ACT_GELU_TANH, "swiglu": TP_ACT_SWIGLU}[act]
+    except KeyError:
+        raise ValueError("act must be 'none', 'gelu_tanh' or 'swiglu'") from None
+    rows = w_shard.shape[0]
+    if a == TP_ACT_SWIGLU and rows % 2:
+        raise ValueError(f"a SwiGLU shard has an even number of rows [gate; up], got {rows}")
+    n = rows // 2 if a == TP_ACT_SWIGLU else rows
     if w_shard.shape[1] != k:
         raise ValueError(f"x is [M, {k}] but w_shard is {tuple(w_shard.shape)}")
-    bias = _vec(bias, "bias", n)
+    bias = _vec(bias, "bias", rows)
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=x.device)
     out = _dev2d(out, "out")
     if tuple(out.shape) != (m, n) or out.dtype not in _DT:
         raise ValueError(f"out must be [{m}, {n}] bf16 or fp32")
-    a = {"none": TP_ACT_NONE, "gelu_tanh": TP_ACT_GELU_TANH}[act]
     _check(lib.tp_linear_colwise(_ptr(x), _ld(x), _ptr(w_shard), _ld(w_shard), _ptr(bias), _ptr(out),
                                  _ld(out), _DT[out.dtype], a, m, n, k, _stream(stream, x)))
     return out

@@ -85,7 +85,8 @@ tp_status check_linear(const char *fn, const void *x, int64_t ldx, const void *w
 
 tp_status run_linear(const char *fn, const tpl::LinearProblem &p, hipStream_t stream)
 {
-    const bool skinny = tpl::gemv_supports(p.M, p.K);
+    // The skinny kernel has no gated epilogue: SwiGLU always takes the tiled kernel.
+    const bool skinny = !p.swiglu && tpl::gemv_supports(p.M, p.K);
     const hipError_t e = skinny ? tpl::launch_gemv(p, stream) : tpl::launch_gemm(p, stream);
     return hip_status(e, fn);
 }
@@ -130,12 +131,17 @@ tp_status tp_linear_colwise(const void *x, int64_t ldx, const void *w_shard, int
     g_msg[0] = 0;
     if (y_dtype != TP_BF16 && y_dtype != TP_F32)
         return fail(TP_ERR_INVALID_ARG, "%s: y_dtype must be TP_BF16 or TP_F32", fn);
-    if (act != TP_ACT_NONE && act != TP_ACT_GELU_TANH)
-        return fail(TP_ERR_INVALID_ARG, "%s: act must be TP_ACT_NONE or TP_ACT_GELU_TANH", fn);
+    if (act != TP_ACT_NONE && act != TP_ACT_GELU_TANH && act != TP_ACT_SWIGLU)
+        return fail(TP_ERR_INVALID_ARG, "%s: act must be TP_ACT_NONE, TP_ACT_GELU_TANH or TP_ACT_SWIGLU", fn);
     bool noop;
     tp_status s = check_linear(fn, x, ldx, w_shard, ldw, bias, y, ldy, elem_size(y_dtype), M, n_shard,
                                K, &noop);
-    if (s != TP_OK || noop)
+    if (s != TP_OK)
+        return s;
+    // SwiGLU reads 2 n_shard weight rows (and bias entries): [gate; up].
+    if (act == TP_ACT_SWIGLU && ((2 * n_shard - 1) * ldw + K) * 2 >= kMaxOperandBytes)
+        return fail(TP_ERR_UNSUPPORTED, "%s: an operand spans 2 GiB or more", fn);
+    if (noop)
         return s;
     tpl::LinearProblem p;
     p.x = (const uint16_t *)x;
@@ -150,6 +156,7 @@ tp_status tp_linear_colwise(const void *x, int64_t ldx, const void *w_shard, int
     p.K = K;
     p.out_bf16 = y_dtype == TP_BF16;
     p.gelu = act == TP_ACT_GELU_TANH;
+    p.swiglu = act == TP_ACT_SWIGLU;
     return run_linear(fn, p, stream);
 }
 

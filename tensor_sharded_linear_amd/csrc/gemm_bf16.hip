@@ -170,10 +170,15 @@ __device__ __forceinline__ void dma16(const char *src, uint16_t *dst)
     __builtin_amdgcn_global_load_lds(src, TPL_LDS(dst), 16, 0, 0);
 }
 
-// acc += X[m0 .. m0+BM-1, k] . W[n0 .. n0+255, k]^T over k-tiles [kt0, kt1).
-// Starts with a barrier, so the LDS may still be in use by the caller's
-// previous tile when it is called.
-template <int TM>
+// acc += X[m0 .. m0+BM-1, k] . Wt^T over k-tiles [kt0, kt1), where the 256
+// rows of the W tile Wt are W[n0 .. n0+255] or, GATED, 32-row blocks taken in
+// turn from the gate half W[0 .. N) and the up half W[N .. 2N) of a packed
+// [gate; up] weight: tile row 64 q + 32 h + i is W[h N + n0 + 32 q + i], so a
+// wave's two 32-column MFMA blocks hold the gate and the up projection of the
+// same 32 output columns n0 + 32 q + [0, 32).  Rows past the end are clamped
+// (computed and discarded).  Starts with a barrier, so the LDS may still be in
+// use by the caller's previous tile when it is called.
+template <int TM, bool GATED>
 __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, const Ctx &c, int m0, int n0,
                                          int kt0, int kt1, f32x16 (&acc)[TM][TN])
 {
@@ -190,7 +195,9 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
     }
 #pragma unroll
     for (int j = 0; j < kDmaW; ++j) {
-        const int gn = min(n0 + j * (8 * kWaves) + c.dma_row, p.N - 1);
+        // DMA instruction j fills tile rows 64 j + dma_row
+        const int gn = GATED ? (c.dma_row >> 5) * p.N + min(n0 + 32 * j + (c.dma_row & 31), p.N - 1)
+                             : min(n0 + j * (8 * kWaves) + c.dma_row, p.N - 1);
         woff[j] = (uint32_t)(((int64_t)gn * p.ldw + c.dma_chunk * 8) * 2);
     }
     auto issue = [&](int stage, int k0) {
@@ -260,20 +267,34 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
 #undef TPL_STEP
 }
 
+// SiLU (Swish): v * sigmoid(v) = v / (1 + exp(-v)); both tails are exact
+// limits (exp -> inf gives -0, exp -> 0 gives v).
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+
+// Epilogue activations.
+constexpr int kActNone = 0;
+constexpr int kActGelu = 1;
+constexpr int kActSwiglu = 2;  // W tile = interleaved [gate; up] 32-row blocks, see mainloop
+
 // Epilogue through LDS.  Lane l holds Y[m][n..n+3] for m = row base +
 // 32 i + l%32 and n = column base + 32 j + 8 q + 4 (l / 32).  For each of
-// the wave's four 32-row slices the wave writes its 32 x 64 values (after
-// bias / GELU / rounding) into a private LDS area with padded rows, then
-// reads them back row-major and stores whole row segments: 4 rows x 256 B
-// (fp32) or 8 rows x 128 B (bf16) per store instruction.
-template <int TM, bool OUT_BF16, bool HAS_BIAS, bool GELU>
+// the wave's 32-row slices the wave writes its output values (after bias /
+// activation / rounding) into a private LDS area with padded rows, then
+// reads them back row-major and stores whole row segments.  A wave owns 64
+// output columns, or 32 with SwiGLU: there its block j = 0 holds the gate and
+// j = 1 the up projection of the same 32 columns, and the output is
+// silu(gate + b_gate) * (up + b_up), the bias being [b_gate; b_up] (2 N).
+template <int TM, bool OUT_BF16, bool HAS_BIAS, int ACT>
 __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, const Ctx &c, int m0, int n0,
                                          const f32x16 (&acc)[TM][TN])
 {
     __syncthreads();  // every wave is done reading the operand stages
     typedef typename std::conditional<OUT_BF16, __bf16, float>::type OutT;
+    constexpr bool kGated = ACT == kActSwiglu;
+    constexpr int WNO = kGated ? 32 : WN;   // output columns per wave
+    constexpr int JO = kGated ? 1 : TN;     // output column blocks per wave
     constexpr int kOutEs = sizeof(OutT);
-    constexpr int kRowElems = WN + 16 / kOutEs;                 // 64 + one 16-byte pad
+    constexpr int kRowElems = WNO + 16 / kOutEs;  // one 16-byte pad per row
     OutT *stage = reinterpret_cast<OutT *>(lds) + c.wave * 32 * kRowElems;
     const int mrow = c.lane & 31;
     const int ncol = 4 * (c.lane >> 5);
@@ -283,31 +304,40 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, con
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             bj[j][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int n = n0 + c.wave_n * WN + j * 32 + q * 8 + ncol;
+            const int n = kGated ? n0 + c.wave_n * WNO + q * 8 + ncol : n0 + c.wave_n * WN + j * 32 + q * 8 + ncol;
             if (HAS_BIAS && n < p.N) {
-                const bf16x4 bb = *reinterpret_cast<const bf16x4 *>(p.bias + n);
+                const bf16x4 bb = *reinterpret_cast<const bf16x4 *>(p.bias + (kGated ? j * p.N + n : n));
                 bj[j][q] = f32x4{(float)bb[0], (float)bb[1], (float)bb[2], (float)bb[3]};
             }
         }
     constexpr int kVec = 16 / kOutEs;              // elements per 16-byte vector
-    constexpr int kVecPerRow = WN / kVec;          // 16 (fp32) or 8 (bf16)
-    constexpr int kRowsPerPass = 64 / kVecPerRow;  // 4 (fp32) or 8 (bf16)
+    constexpr int kVecPerRow = WNO / kVec;
+    constexpr int kRowsPerPass = 64 / kVecPerRow;
     const int rd_row = c.lane / kVecPerRow;
     const int rd_vec = c.lane % kVecPerRow;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < JO; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 f32x4 v = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
                 if (HAS_BIAS)
                     v = v + bj[j][q];
-                if (GELU) {
+                if (ACT == kActGelu) {
                     v[0] = gelu_tanh(v[0]);
                     v[1] = gelu_tanh(v[1]);
                     v[2] = gelu_tanh(v[2]);
                     v[3] = gelu_tanh(v[3]);
+                }
+                if (kGated) {
+                    f32x4 u = f32x4{acc[i][1][4 * q], acc[i][1][4 * q + 1], acc[i][1][4 * q + 2], acc[i][1][4 * q + 3]};
+                    if (HAS_BIAS)
+                        u = u + bj[1][q];
+                    v[0] = silu(v[0]) * u[0];
+                    v[1] = silu(v[1]) * u[1];
+                    v[2] = silu(v[2]) * u[2];
+                    v[3] = silu(v[3]) * u[3];
                 }
                 OutT *dst = stage + mrow * kRowElems + j * 32 + q * 8 + ncol;
                 if (OUT_BF16)
@@ -316,7 +346,7 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, con
                     *reinterpret_cast<f32x4 *>(dst) = v;
             }
         const int mbase = m0 + c.wave_m * Tile<TM>::WM + i * 32;
-        const int ncol0 = n0 + c.wave_n * WN + rd_vec * kVec;
+        const int ncol0 = n0 + c.wave_n * WNO + rd_vec * kVec;
 #pragma unroll
         for (int r = 0; r < 32; r += kRowsPerPass) {
             const int row = r + rd_row;
@@ -340,37 +370,40 @@ __device__ __forceinline__ void zero(f32x16 (&acc)[TM][TN])
                 acc[i][j][e] = 0.f;
 }
 
-// One BM x 256 output tile per workgroup.
-template <int TM, bool OUT_BF16, bool HAS_BIAS, bool GELU>
+// One BM x 256 output tile per workgroup (BM x 128 output columns with
+// SwiGLU: the tile's 256 weight rows are 128 gate and 128 up rows).
+template <int TM, bool OUT_BF16, bool HAS_BIAS, int ACT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_nt_kernel(GemmParams p)
 {
     constexpr int BM = Tile<TM>::BM;
+    constexpr bool kGated = ACT == kActSwiglu;
+    constexpr int kTileCols = kGated ? BN / 2 : BN;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[Tile<TM>::kLdsElems];
     const Ctx c = make_ctx<TM>();
     int tm, tn;
     tile_of(xcd_contiguous(blockIdx.x, p.tiles_m * p.tiles_n), p, tm, tn);
     f32x16 acc[TM][TN];
     zero<TM>(acc);
-    mainloop<TM>(p, lds, c, tm * BM, tn * BN, 0, p.K / BK, acc);
-    epilogue<TM, OUT_BF16, HAS_BIAS, GELU>(p, lds, c, tm * BM, tn * BN, acc);
+    mainloop<TM, kGated>(p, lds, c, tm * BM, tn * kTileCols, 0, p.K / BK, acc);
+    epilogue<TM, OUT_BF16, HAS_BIAS, ACT>(p, lds, c, tm * BM, tn * kTileCols, acc);
 }
 
-template <int TM, bool OUT_BF16, bool HAS_BIAS, bool GELU>
+template <int TM, bool OUT_BF16, bool HAS_BIAS, int ACT>
 hipError_t launch_tm(GemmParams gp, hipStream_t stream)
 {
     gp.tiles_m = (gp.M + Tile<TM>::BM - 1) / Tile<TM>::BM;
     gp.group_m = gp.tiles_m < 8 ? gp.tiles_m : 8;
-    hipLaunchKernelGGL((gemm_bf16_nt_kernel<TM, OUT_BF16, HAS_BIAS, GELU>), dim3(gp.tiles_m * gp.tiles_n),
+    hipLaunchKernelGGL((gemm_bf16_nt_kernel<TM, OUT_BF16, HAS_BIAS, ACT>), dim3(gp.tiles_m * gp.tiles_n),
                        dim3(kThreads), 0, stream, gp);
     return hipGetLastError();
 }
 
-template <bool OUT_BF16, bool HAS_BIAS, bool GELU>
+template <bool OUT_BF16, bool HAS_BIAS, int ACT>
 hipError_t launch_variant(const GemmParams &gp, int tm, hipStream_t stream)
 {
-    return tm == 3 ? launch_tm<3, OUT_BF16, HAS_BIAS, GELU>(gp, stream)
-                   : launch_tm<4, OUT_BF16, HAS_BIAS, GELU>(gp, stream);
+    return tm == 3 ? launch_tm<3, OUT_BF16, HAS_BIAS, ACT>(gp, stream)
+                   : launch_tm<4, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
 }
 
 // Compute units of the current device (cached per device).
@@ -416,19 +449,25 @@ hipError_t launch_gemm(const LinearProblem &pr, hipStream_t stream)
     gp.M = (int)pr.M;
     gp.N = (int)pr.N;
     gp.K = (int)pr.K;
-    gp.tiles_n = (int)((pr.N + BN - 1) / BN);
+    const int act = pr.swiglu ? kActSwiglu : (pr.gelu ? kActGelu : kActNone);
+    const int tile_cols = pr.swiglu ? BN / 2 : BN;
+    gp.tiles_n = (int)((pr.N + tile_cols - 1) / tile_cols);
     const int tm = pick_tm(gp.M, gp.tiles_n, cu_count());
     const bool bias = pr.bias != nullptr;
-    const int sel = (pr.out_bf16 ? 4 : 0) | (bias ? 2 : 0) | (pr.gelu ? 1 : 0);
-    switch (sel) {
-    case 0: return launch_variant<false, false, false>(gp, tm, stream);
-    case 1: return launch_variant<false, false, true>(gp, tm, stream);
-    case 2: return launch_variant<false, true, false>(gp, tm, stream);
-    case 3: return launch_variant<false, true, true>(gp, tm, stream);
-    case 4: return launch_variant<true, false, false>(gp, tm, stream);
-    case 5: return launch_variant<true, false, true>(gp, tm, stream);
-    case 6: return launch_variant<true, true, false>(gp, tm, stream);
-    default: return launch_variant<true, true, true>(gp, tm, stream);
+    const int sel = (pr.out_bf16 ? 6 : 0) + (bias ? 3 : 0);
+    switch (sel + act) {
+    case 0: return launch_variant<false, false, 0>(gp, tm, stream);
+    case 1: return launch_variant<false, false, 1>(gp, tm, stream);
+    case 2: return launch_variant<false, false, 2>(gp, tm, stream);
+    case 3: return launch_variant<false, true, 0>(gp, tm, stream);
+    case 4: return launch_variant<false, true, 1>(gp, tm, stream);
+    case 5: return launch_variant<false, true, 2>(gp, tm, stream);
+    case 6: return launch_variant<true, false, 0>(gp, tm, stream);
+    case 7: return launch_variant<true, false, 1>(gp, tm, stream);
+    case 8: return launch_variant<true, false, 2>(gp, tm, stream);
+    case 9: return launch_variant<true, true, 0>(gp, tm, stream);
+    case 10: return launch_variant<true, true, 1>(gp, tm, stream);
+    default: return launch_variant<true, true, 2>(gp, tm, stream);
     }
 }
 

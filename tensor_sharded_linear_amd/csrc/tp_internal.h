@@ -22,6 +22,7 @@ struct LinearProblem {
     int64_t M, N, K;
     bool out_bf16;
     bool gelu;
+    bool swiglu = false;  // W holds 2N rows [gate; up]; y = silu(x gate^T + b_g) * (x up^T + b_u)
 };
 
 // Tiled MFMA GEMM (M > kSkinnyMaxM).  Requires K % 64 == 0, N % 16 == 0.

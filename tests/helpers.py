@@ -98,3 +98,41 @@ def sample_rows(m: int, n_random: int, seed: int, tile: int = 256) -> np.ndarray
     rng = np.random.default_rng(seed)
     rows.update(rng.integers(0, m, size=n_random).tolist())
     return np.array(sorted(r for r in rows if 0 <= r < m), dtype=np.int64)
+
+
+def check_swiglu(gpu, x_bits, w_bits, b_bits, out_bf16, rows=None, what=""):
+    """SwiGLU output against the oracle: the stated bar (rel-L2; max-abs beyond the output
+    rounding), then a bound
+    propagated from the two halves' accumulation errors E_g, E_u (as in check_close):
+    |d out| <= 1.1 E_g (|u| + E_u) + |silu(g)| E_u, since |silu'| <= 1.1; plus the fp32
+    evaluation of silu and of the product (a few ulp of the result) and the output rounding."""
+    import oracle
+    n = w_bits.shape[0] // 2
+    xs = x_bits if rows is None else x_bits[rows]
+    k = x_bits.shape[1]
+    bg = bu = None
+    if b_bits is not None:
+        bg, bu = b_bits[:n], b_bits[n:]
+    ref = oracle.colwise_swiglu(x_bits, w_bits, b_bits, rows=rows)
+    g = oracle.linear(x_bits, np.ascontiguousarray(w_bits[:n]), bg, rows=rows)
+    u = oracle.linear(x_bits, np.ascontiguousarray(w_bits[n:]), bu, rows=rows)
+    e_g = 1.2 * gamma(k + 2) * abs_dot(xs, w_bits[:n], bg) + 1e-6
+    e_u = 1.2 * gamma(k + 2) * abs_dot(xs, w_bits[n:], bu) + 1e-6
+    with np.errstate(over="ignore"):
+        sg = np.abs(g / (1.0 + np.exp(-g)))
+    gpu = np.asarray(gpu, np.float64)
+    assert gpu.shape == ref.shape and np.all(np.isfinite(gpu)), what
+    err = np.abs(gpu - ref)
+    mag = np.maximum(np.abs(ref), np.abs(gpu))
+    hu = half_ulp_bf16(mag) if out_bf16 else half_ulp_f32(mag)
+    # SwiGLU outputs reach |y| >= 8, where half a bf16 ulp (1/32) alone exceeds the
+    # max-abs bar: the bar is applied to the error beyond the output rounding.
+    beyond = float((err - hu).max()) if err.size else 0.0
+    assert beyond <= MAX_ABS, f"{what}: max abs error beyond output rounding {beyond} > {MAX_ABS}"
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(gpu - ref)) / nref if nref > 0 else float(np.linalg.norm(gpu - ref))
+    assert rel <= MAX_REL_L2, f"{what}: rel L2 error {rel} > {MAX_REL_L2}"
+    bound = hu + 1.1 * e_g * (np.abs(u) + e_u) + sg * e_u + 8 * U32 * mag + 1e-7
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements beyond the derived SwiGLU bound; "
+                           f"worst excess {float((err - bound).max())}")

@@ -91,6 +91,14 @@ def test_colwise_validation(kw, status):
     assert tsl.tp_last_error().startswith("tp_linear_colwise")
 
 
+def test_swiglu_weight_extent_counts_both_halves():
+    """A SwiGLU shard reads 2 n_shard weight rows: n rows fit under 2 GiB, 2 n do not."""
+    n, k = 1 << 18, 1 << 11
+    st = colwise(N=n, ldy=n, K=k, ldx=k, ldw=k, act=B.TP_ACT_SWIGLU)
+    assert st == B.TP_ERR_UNSUPPORTED
+    assert "2 GiB" in tsl.tp_last_error()
+
+
 def test_colwise_and_rowwise_empty_is_noop():
     assert colwise(M=0, x=None, y=None) == B.TP_OK
     assert rowwise(M=0, x=None, p=None) == B.TP_OK

@@ -333,6 +333,83 @@ def test_rowwise_split_input_checks_the_plan():
 
 
 # --------------------------------------------------------------------------------------
+# SwiGLU of a packed [gate; up] projection
+# --------------------------------------------------------------------------------------
+
+def _gate_up(rng, m, n, k, gate_lo, gate_hi):
+    """Integer inputs with every gate pre-activation in k*[gate_lo, gate_hi]*[1, 3]."""
+    x = si.int_bf16(rng, (m, k), 1, 3)
+    g = si.int_bf16(rng, (n, k), gate_lo, gate_hi)
+    u = si.int_bf16(rng, (n, k), -4, 4)
+    return x, np.concatenate([g, u])
+
+
+def test_swiglu_zero_gate_is_zero():
+    """silu(0) = 0: a zero gate half gives exactly 0 whatever the up half."""
+    rng = np.random.default_rng(100)
+    x = si.normal_bf16(rng, (5, 64))
+    w = np.concatenate([np.zeros((7, 64), np.uint16), si.normal_bf16(rng, (7, 64))])
+    assert np.all(oracle.colwise_swiglu(x, w) == 0.0)
+
+
+def test_swiglu_saturated_gate_is_gate_times_up():
+    """A gate pre-activation >= 64 has silu(g) = g to double precision (e^-64 < 2^-53), so
+    the output is exactly g * u.  Gate first, up second: swapping the halves, or a missing
+    product, fails this."""
+    rng = np.random.default_rng(101)
+    m, n, k = 6, 9, 64
+    x, w = _gate_up(rng, m, n, k, 1, 4)
+    g = oracle.linear(x, w[:n])
+    u = oracle.linear(x, w[n:])
+    assert g.min() >= 64
+    assert np.array_equal(oracle.colwise_swiglu(x, w), g * u)
+
+
+def test_swiglu_saturated_negative_gate_vanishes():
+    rng = np.random.default_rng(102)
+    m, n, k = 4, 5, 64
+    x, w = _gate_up(rng, m, n, k, -4, -1)
+    assert oracle.linear(x, w[:n]).max() <= -64
+    assert np.all(np.abs(oracle.colwise_swiglu(x, w)) < 1e-20)
+
+
+def test_swiglu_unit_gate_is_sigmoid_of_one():
+    """g = 1 exactly (one-hot input, unit gate weight): output = sigma(1) * u,
+    sigma(1) = 0.7310585786300049."""
+    k = 64
+    x = np.zeros((1, k), np.uint16)
+    x[0, 3] = 0x3F80                      # 1.0
+    gate = np.zeros((1, k), np.uint16)
+    gate[0, 3] = 0x3F80
+    up = np.zeros((1, k), np.uint16)
+    up[0, 3] = 0x4040                     # 3.0
+    out = oracle.colwise_swiglu(x, np.concatenate([gate, up]))
+    assert abs(out[0, 0] - 3 * 0.7310585786300049) < 1e-15
+
+
+@pytest.mark.parametrize("P", [1, 2, 4])
+def test_swiglu_packed_shards_concat_equals_unsharded(P):
+    """[TP] "Fused projections": blocks [1, 1] shard the gate and the up halves
+    independently, so rank r's shard pairs its gate rows with the matching up rows and
+    the ranks' outputs, side by side, are the unsharded output.  Plain colwise slicing
+    of the packed weight misaligns gate and up."""
+    rng = np.random.default_rng(110 + P)
+    m, n, k = 7, 16, 64
+    x = si.normal_bf16(rng, (m, k))
+    w = si.normal_bf16(rng, (2 * n, k), 1 / 8)
+    b = si.normal_bf16(rng, (2 * n,))
+    full = oracle.colwise_swiglu(x, w, b)
+    outs = []
+    for r in range(P):
+        ws, bs = oracle.shard_packed_colwise(w, b, [1, 1], P, r)
+        outs.append(oracle.colwise_swiglu(x, ws, bs))
+    assert np.array_equal(np.concatenate(outs, axis=1), full)
+    if P > 1:
+        ws, bs = oracle.shard_colwise(w, b, P, 0)
+        assert not np.allclose(oracle.colwise_swiglu(x, ws, bs), full[:, :n // P])
+
+
+# --------------------------------------------------------------------------------------
 # slicing
 # --------------------------------------------------------------------------------------
 
