@@ -110,6 +110,36 @@ def reduce_traffic(fetch_dir, write_dir, probe_json):
     }
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
+    fe, wr = res["fetch"], res["write"]
+    alg_w = wr["bytes_per_launch"]  # measured writes: equal to the output bytes on these shapes
+    md = [
+        f"# HBM-side traffic of gemm_bf16_nt_kernel over one bench step ({probe['gemm_launches_per_step']} "
+        "GEMM launches)", "",
+        "Commands (run from the repository root on one MI355X; each counter in its own run):", "", "```",
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/tr_fetch -o run -- "
+        "python3 bench.py --probe gpurun_out/probe_f.json",
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/tr_write -o run -- "
+        "python3 bench.py --probe gpurun_out/probe.json",
+        "python3 bench.py --traffic gpurun_out/tr_fetch gpurun_out/tr_write gpurun_out/probe.json",
+        "```", "",
+        f"`--probe` runs two bench steps untimed, then one `copy_segments_kernel` copy of a {CAL_ROWS} x "
+        f"{CAL_COLS} bf16 weight ({probe['cal_bytes']} bytes read, the same written) as the calibration of "
+        "known size.  The figures are for the GEMM source with hash "
+        f"`{out['source_sha']}`.", "",
+        "| counter | calibration copy reads | factor | GEMM, per launch (last step) | scaled |",
+        "|---|---|---|---|---|",
+        f"| FETCH_SIZE | {fe['calibration_kib']:.0f} KiB (true {probe['cal_bytes'] / 1024:.0f} KiB) | "
+        f"{fe['factor']:.4f} | {fe['kib_per_launch']:.0f} KiB | {fe['bytes_per_launch'] / 1e6:.1f} MB |",
+        f"| WRITE_SIZE | {wr['calibration_kib']:.0f} KiB (true {probe['cal_bytes'] / 1024:.0f} KiB) | "
+        f"{wr['factor']:.4f} | {wr['kib_per_launch']:.0f} KiB | {wr['bytes_per_launch'] / 1e6:.1f} MB |", "",
+        f"Traffic {total / 1e6:.1f} MB per launch against {probe['alg_bytes_per_launch'] / 1e6:.1f} MB "
+        f"algorithmic (X and W read once, Y written once): {total / probe['alg_bytes_per_launch']:.2f}x.  "
+        f"Operand reads are {fe['bytes_per_launch'] / (probe['alg_bytes_per_launch'] - alg_w):.2f}x the "
+        "operand bytes, taking the writes as the output bytes: each XCD's L2 fetches every X and W panel "
+        "that its concurrent tiles touch.",
+    ]
+    with open(os.path.join(ROOT, "profiles", "gemm_traffic.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
     print(json.dumps(out))
 
 
