@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--detail", action="store_true", help="also print a per-shape GEMM table to stderr")
+    ap.add_argument("--streams", type=int, default=1, choices=(1, 2),
+                    help="2: slicing and combines on a second stream beside the GEMMs (measured slower)")
     ap.add_argument("--probe", metavar="OUT_JSON",
                     help="untimed: two steps, then a calibration copy of known size, for rocprofv3 --pmc "
                          "FETCH_SIZE / WRITE_SIZE runs; writes the step's algorithmic GEMM bytes to OUT_JSON")
@@ -151,14 +153,17 @@ class Timer:
         self.on = False
         self.rec = []  # (category, key, work, bytes, ev0, ev1)
 
-    def run(self, cat, key, flops, nbytes, fn):
-        if not self.on:
-            return fn()
-        e0 = self.torch.cuda.Event(enable_timing=True)
-        e1 = self.torch.cuda.Event(enable_timing=True)
-        e0.record()
-        out = fn()
-        e1.record()
+    def run(self, cat, key, flops, nbytes, fn, stream=None):
+        """Launch fn on `stream` (torch's current stream if None), timed by events on it."""
+        s = stream if stream is not None else self.torch.cuda.current_stream()
+        with self.torch.cuda.stream(s):
+            if not self.on:
+                return fn()
+            e0 = self.torch.cuda.Event(enable_timing=True)
+            e1 = self.torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            out = fn()
+            e1.record(s)
         self.rec.append((cat, key, flops, nbytes, e0, e1))
         return out
 
@@ -271,73 +276,111 @@ def main():
     def gemm_cost(m_, n_, k_, out_es):
         return 2.0 * m_ * n_ * k_, 2.0 * (m_ * k_ + n_ * k_) + out_es * m_ * n_
 
+    # Two streams: the index and combine kernels (HBM-bound) run on `cs` and overlap
+    # the GEMMs (MFMA-bound) on `ms`; events carry every producer -> consumer and
+    # reader -> next writer dependency between them, across steps too.
+    ms = torch.cuda.current_stream()
+    cs = torch.cuda.Stream(device=dev) if args.streams > 1 else ms
+    two = cs is not ms
+    ev = {}
+
+    def wait(stream, key):
+        if two and key in ev:
+            stream.wait_event(ev[key])
+
+    def mark(stream, key):
+        if two:
+            e = torch.cuda.Event()
+            e.record(stream)
+            ev[key] = e
+
     def step():
         for P in tps:
             b = bufs[P]
             kq = 3 * H // P * hd
             # shard every weight for every rank (index kernels)
             for r in range(P):
+                wait(cs, ("w read", P, r))
                 T.run("slice", "qkv", 0, 2 * 2 * kq * hidden,
-                      lambda: tsl.tp_fused_qkv_split(wqkv, None, H, hd, P, r, w_out=b["wq"][r]))
+                      lambda: tsl.tp_fused_qkv_split(wqkv, None, H, hd, P, r, w_out=b["wq"][r]), cs)
                 T.run("slice", "wo", 0, 2 * 2 * hidden * hidden // P,
-                      lambda: tsl.tp_plan_shard_slice(wo, None, "rowwise", P, r, w_out=b["wo"][r]))
+                      lambda: tsl.tp_plan_shard_slice(wo, None, "rowwise", P, r, w_out=b["wo"][r]), cs)
                 T.run("slice", "w1", 0, 2 * 2 * ffn // P * hidden,
-                      lambda: tsl.tp_plan_shard_slice(w1, None, "colwise", P, r, w_out=b["w1"][r]))
+                      lambda: tsl.tp_plan_shard_slice(w1, None, "colwise", P, r, w_out=b["w1"][r]), cs)
                 T.run("slice", "w2", 0, 2 * 2 * hidden * ffn // P,
-                      lambda: tsl.tp_plan_shard_slice(w2, None, "rowwise", P, r, w_out=b["w2"][r]))
+                      lambda: tsl.tp_plan_shard_slice(w2, None, "rowwise", P, r, w_out=b["w2"][r]), cs)
+                mark(cs, ("w ready", P, r))
             # every rank's projections
             k_loc = hidden // P
+            wait(ms, ("out read", P))
             for r in range(P):
+                wait(ms, ("w ready", P, r))
                 f, by = gemm_cost(M, kq, hidden, 2)
                 T.run("gemm", f"colwise {M}x{kq}x{hidden}", f, by,
-                      lambda: tsl.tp_linear_colwise(x, b["wq"][r], out=b["q"][r]))
+                      lambda: tsl.tp_linear_colwise(x, b["wq"][r], out=b["q"][r]), ms)
                 f, by = gemm_cost(M, hidden, k_loc, 4)
                 T.run("gemm", f"rowwise {M}x{hidden}x{k_loc}", f, by,
                       lambda: tsl.tp_linear_rowwise(A[:, r * k_loc:(r + 1) * k_loc], b["wo"][r],
-                                                    out=b["po"][r]))
+                                                    out=b["po"][r]), ms)
                 f, by = gemm_cost(M, ffn // P, hidden, 2)
                 T.run("gemm", f"colwise+gelu {M}x{ffn // P}x{hidden}", f, by,
-                      lambda: tsl.tp_linear_colwise(x, b["w1"][r], act="gelu_tanh", out=b["h"][r]))
+                      lambda: tsl.tp_linear_colwise(x, b["w1"][r], act="gelu_tanh", out=b["h"][r]), ms)
                 f, by = gemm_cost(M, hidden, ffn // P, 4)
                 T.run("gemm", f"rowwise {M}x{hidden}x{ffn // P}", f, by,
-                      lambda: tsl.tp_linear_rowwise(b["h"][r], b["w2"][r], out=b["pd"][r]))
+                      lambda: tsl.tp_linear_rowwise(b["h"][r], b["w2"][r], out=b["pd"][r]), ms)
+                mark(ms, ("w read", P, r))
+            mark(ms, ("out ready", P))
             # layer-boundary combines
+            wait(cs, ("out ready", P))
             T.run("sum", f"P{P} f32", 0, (P + 1) * 4.0 * M * hidden,
-                  lambda: tsl.tp_partial_combine(b["po"], "sum", out=b["out_sum"]))
+                  lambda: tsl.tp_partial_combine(b["po"], "sum", out=b["out_sum"]), cs)
             T.run("sum", f"P{P} bf16", 0, (P * 4.0 + 2.0) * M * hidden,
-                  lambda: tsl.tp_partial_combine(b["pd"], "sum", out=b["down_sum"]))
+                  lambda: tsl.tp_partial_combine(b["pd"], "sum", out=b["down_sum"]), cs)
             T.run("concat", "qkv", 0, 2 * 2.0 * M * 3 * H * hd,
-                  lambda: tsl.tp_partial_combine(b["q"], "concat", blocks=[1, 1, 1], out=b["q_cat"]))
+                  lambda: tsl.tp_partial_combine(b["q"], "concat", blocks=[1, 1, 1], out=b["q_cat"]), cs)
             T.run("concat", "up", 0, 2 * 2.0 * M * ffn,
-                  lambda: tsl.tp_partial_combine(b["h"], "concat", out=b["h_cat"]))
+                  lambda: tsl.tp_partial_combine(b["h"], "concat", out=b["h_cat"]), cs)
+            mark(cs, ("out read", P))
         # fused gate/up projection with SwiGLU: packed [1, 1] slices, then each rank's GEMM
         for r in range(P_GU):
+            wait(cs, ("gu read", r))
             T.run("slice", "w_gu [1,1]", 0, 2 * 2 * 2 * n_gu * hidden,
                   lambda: tsl.tp_plan_shard_slice(w_gu, b_gu, "colwise", P_GU, r, blocks=[1, 1],
-                                                  w_out=gu_w[r], b_out=gu_b[r]))
+                                                  w_out=gu_w[r], b_out=gu_b[r]), cs)
+            mark(cs, ("gu ready", r))
         for r in range(P_GU):
+            wait(ms, ("gu ready", r))
             f, by = gemm_cost(M, 2 * n_gu, hidden, 0)
             T.run("gemm", f"colwise+swiglu {M}x{2 * n_gu}x{hidden}", f, by + 2.0 * M * n_gu,
-                  lambda: tsl.tp_linear_colwise(x_gu, gu_w[r], gu_b[r], act="swiglu", out=gu_y[r]))
+                  lambda: tsl.tp_linear_colwise(x_gu, gu_w[r], gu_b[r], act="swiglu", out=gu_y[r]), ms)
+            mark(ms, ("gu read", r))
         # adaLN modulation: shard for 4 ranks, then each rank's skinny GEMV
         for r in range(P_ADA):
+            wait(cs, ("ada read", r))
             T.run("slice", "w_ada", 0, 2 * 2 * n_ada * hidden,
-                  lambda: tsl.tp_plan_shard_slice(w_ada, None, "colwise", P_ADA, r, w_out=ada_w[r]))
+                  lambda: tsl.tp_plan_shard_slice(w_ada, None, "colwise", P_ADA, r, w_out=ada_w[r]), cs)
+            mark(cs, ("ada ready", r))
         for r in range(P_ADA):
+            wait(ms, ("ada ready", r))
             T.run("gemv", f"adaLN B{B_ADA} {n_ada}x{hidden}", 2.0 * B_ADA * n_ada * hidden,
                   2.0 * n_ada * hidden + 2.0 * B_ADA * (hidden + n_ada),
-                  lambda: tsl.tp_linear_colwise(c_ada, ada_w[r], out=ada_y[r]))
+                  lambda: tsl.tp_linear_colwise(c_ada, ada_w[r], out=ada_y[r]), ms)
+            mark(ms, ("ada read", r))
         # adaLN modulation, rowwise_split_input: shard, each rank's partial from its input slice, SUM
         for r in range(P_ADA):
+            wait(cs, ("adas read", r))
             T.run("slice", "w_ada split", 0, 2 * 2 * n_full_ada * k_ada,
                   lambda: tsl.tp_plan_shard_slice(w_ada, None, "rowwise_split_input", P_ADA, r,
-                                                  w_out=ada_ws[r]))
+                                                  w_out=ada_ws[r]), cs)
+            mark(cs, ("adas ready", r))
         for r in range(P_ADA):
+            wait(ms, ("adas ready", r))
             T.run("gemv", f"adaLN split-input B{B_ADA} {n_full_ada}x{k_ada}", 2.0 * B_ADA * n_full_ada * k_ada,
                   2.0 * n_full_ada * k_ada + 2.0 * B_ADA * k_ada + 4.0 * B_ADA * n_full_ada,
-                  lambda: tsl.tp_linear_rowwise_split_input(c_ada, ada_ws[r], P_ADA, r, out=ada_p[r]))
+                  lambda: tsl.tp_linear_rowwise_split_input(c_ada, ada_ws[r], P_ADA, r, out=ada_p[r]), ms)
+            mark(ms, ("adas read", r))
         T.run("sum", f"adaLN P{P_ADA} bf16", 0, (P_ADA * 4.0 + 2.0) * B_ADA * n_full_ada + 2.0 * n_full_ada,
-              lambda: tsl.tp_partial_combine(ada_p, "sum", bias=b_ada, out=ada_sum))
+              lambda: tsl.tp_partial_combine(ada_p, "sum", bias=b_ada, out=ada_sum), ms)
 
     for P in tps:
         gemm_flops_step += P * 2.0 * M * hidden * (3 * H // P * hd + ffn // P) + \
@@ -415,7 +458,8 @@ def main():
                         "+ adaLN 6144->36864 at tp 4, 4 rows, colwise and rowwise_split_input",
             "tokens": M, "hidden": hidden, "ffn": ffn, "heads": H, "head_dim": hd,
             "tp_degrees": tps, "adaln_rows": B_ADA, "adaln_tp": P_ADA,
-            "parallelism": "tp shares computed sequentially on 1 GPU",
+            "parallelism": "tp shares computed sequentially on 1 GPU" + (
+                "; slicing and combines on a second HIP stream, overlapping the GEMMs" if args.streams > 1 else ""),
         },
         "roofline": {
             "kernel": "gemm_bf16_nt_kernel",
