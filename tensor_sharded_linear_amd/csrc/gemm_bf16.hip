@@ -2,7 +2,7 @@
 //
 // Computes Y = epilogue(X . W^T) with X [M, K] and W [N, K] both K-contiguous
 // (nn.Linear layout), fp32 accumulation on the CDNA4 matrix cores
-// (v_mfma_f32_32x32x16_bf16), and a fused epilogue: + bias, GELU-tanh, store
+// (v_mfma_f32_16x16x32_bf16), and a fused epilogue: + bias, GELU-tanh, store
 // as bf16 (round to nearest even) or fp32.  The colwise shard of the
 // Diffusers "Tensor parallelism" page (section "Colwise and rowwise") is this
 // kernel on a row block of W; the rowwise shard is this kernel on a column
@@ -10,31 +10,38 @@
 //
 // Design for gfx950:
 //  * 256 x 256 output tile per workgroup, K step 64, 512 threads = 8 waves in
-//    a 2 (M) x 4 (N) grid; each wave owns a 128 x 64 sub-tile held as 4 x 2
-//    MFMA 32x32 fp32 accumulators (128 accumulator registers per lane).  Two
+//    a 2 (M) x 4 (N) grid; each wave owns a 128 x 64 sub-tile held as 8 x 4
+//    MFMA 16x16 fp32 accumulators (128 accumulator registers per lane).  Two
 //    waves per SIMD, so one wave's LDS fragment reads overlap the other's
 //    MFMAs; one wave per SIMD left the LDS read port idle half the time.
+//  * The part runs at its power limit on dense random operands (the same
+//    kernel on all-zero operands is about 35% faster), so energy per flop
+//    sets the speed.  Counting operand reads plus accumulator read and write,
+//    the 16x16x32 form moves 20% fewer register bytes per flop than
+//    32x32x16, and it measured 3-9% faster on every workload shape.
 //  * Operands go HBM/L2 -> LDS by direct-to-LDS DMA (global_load_lds_dwordx4),
 //    no VGPR staging, double-buffered: 2 stages x (X tile + W tile) x 32 KiB =
 //    128 KiB of the 160 KiB LDS.
-//  * Fragments are double-buffered in registers at k16 granularity: while
-//    the 8 MFMAs of one k16 step run, the 6 fragments of the next step are
-//    read from LDS.  The single barrier per k-tile sits before the last k16
-//    step: after it the next k-tile has landed and every wave has finished
+//  * Fragments are double-buffered in registers at k32 granularity: while
+//    the 32 MFMAs of one k32 step run, the 12 fragments of the next step are
+//    read from LDS, one read after each of the first 12 MFMAs.  The single
+//    barrier per k-tile sits before the second k32 step: after it the next
+//    k-tile has landed and every wave has finished
 //    reading the stage that the DMA for the k-tile after next then
 //    overwrites, so the DMA runs a whole k-tile ahead and no fragment read is
 //    exposed.
 //  * LDS tiles are 64-element (128-byte) rows; the 16-byte chunk c of row r
 //    is stored at position c ^ ((r >> 1) & 7).  A fragment read covers 32
-//    rows of one chunk column; under this swizzle each group of lanes that
-//    the LDS serves together touches distinct banks.
+//    16 rows of one chunk column per 16 lanes; under this swizzle each group
+//    of lanes that the LDS serves together touches distinct banks.
 //  * The W fragment is the MFMA "A" operand and the X fragment the "B"
 //    operand, so each lane holds runs of four consecutive output columns of
 //    one row.  The epilogue applies bias / GELU / rounding, passes each
-//    32-row slice of a wave's tile through a private LDS area and stores
+//    16-row slice of a wave's tile through a private LDS area and stores
 //    whole row segments (4 rows x 256 B fp32, 8 rows x 128 B bf16 per
-//    instruction): direct stores from the MFMA layout cover 32 rows x 32 B
-//    and measured 1.64x the algorithmic write bytes for an fp32 output.
+//    instruction): direct stores from the MFMA layout cover 16 rows x 16 B
+//    per instruction and wrote 1.64x the algorithmic bytes for an fp32
+//    output when measured with the 32x32 layout.
 //  * Workgroups are dealt round-robin to the 8 XCDs; the tile index is
 //    remapped so each XCD gets a contiguous run of a grouped raster order,
 //    which keeps its concurrent tiles on few X row-panels and W row-panels
@@ -51,7 +58,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 #define TPL_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
@@ -64,11 +70,12 @@ constexpr int kThreads = 512;     // 8 waves in a 2 (M) x 4 (N) grid
 constexpr int kWavesN = 4;
 constexpr int kWaves = kThreads / 64;
 constexpr int WN = 64;            // columns of the output owned by one wave
-constexpr int TN = WN / 32;       // 32-column MFMA tiles per wave
+constexpr int WB = WN / 16;       // 16-row W blocks (16-column MFMA tiles) per wave
 constexpr int kDmaW = (BN * BK * 2) / (kThreads * 16);  // 16-byte DMAs per thread per W tile
 
 template <int TM>
 struct Tile {
+    static constexpr int XB = 2 * TM;    // 16-row X blocks (16-row MFMA tiles) per wave
     static constexpr int WM = 32 * TM;   // rows of the output owned by one wave
     static constexpr int BM = 2 * WM;    // rows of the output tile
     static constexpr int kDmaX = (BM * BK * 2) / (kThreads * 16);  // 16-byte DMAs per thread per X tile
@@ -121,12 +128,12 @@ __device__ __forceinline__ float gelu_tanh(float v)
     return v / (1.0f + __expf(-2.0f * u));
 }
 
-// One k16 step's operand fragments: per lane 8 bf16 of one row of each of
-// the wave's TM 32-row X blocks and two 32-row W blocks.
+// One k32 step's operand fragments: per lane 8 bf16 of one row of each of
+// the wave's 2 TM 16-row X blocks and four 16-row W blocks.
 template <int TM>
 struct Frags {
-    bf16x8 x[TM];
-    bf16x8 w[TN];
+    bf16x8 x[Tile<TM>::XB];
+    bf16x8 w[WB];
 };
 
 // Per-thread constants of the tile pipeline.
@@ -134,7 +141,7 @@ struct Ctx {
     int lane, wave, wave_m, wave_n;
     int dma_row, dma_chunk;       // DMA: row within a 64-row group, logical chunk
     int xrow_off, wrow_off;       // fragment row offsets inside an LDS tile
-    int swz, kh;                  // fragment swizzle and k-half
+    int swz, kh;                  // fragment swizzle and k-quarter
 };
 
 template <int TM>
@@ -152,13 +159,13 @@ __device__ __forceinline__ Ctx make_ctx()
     // (l%8) ^ ((R >> 1) & 7) = (l%8) ^ ((4 (w & 1) + l/16) & 7).
     c.dma_row = c.wave * 8 + (c.lane >> 3);
     c.dma_chunk = (c.lane & 7) ^ ((((c.wave & 1) << 2) + (c.lane >> 4)) & 7);
-    // Fragment addressing: lane l reads row (l % 32) of a 32-row block,
-    // 16-byte k-chunk (2 s + l / 32) for k16 step s, stored at position
-    // chunk ^ ((row >> 1) & 7) = chunk ^ ((l >> 1) & 7).
-    c.xrow_off = (c.wave_m * Tile<TM>::WM + (c.lane & 31)) * BK;
-    c.wrow_off = (c.wave_n * WN + (c.lane & 31)) * BK;
+    // Fragment addressing: lane l reads row (l % 16) of a 16-row block,
+    // 16-byte k-chunk (4 s + l / 16) for k32 step s, stored at position
+    // chunk ^ ((row >> 1) & 7) = chunk ^ (((l % 16) >> 1) & 7).
+    c.xrow_off = (c.wave_m * Tile<TM>::WM + (c.lane & 15)) * BK;
+    c.wrow_off = (c.wave_n * WN + (c.lane & 15)) * BK;
     c.swz = (c.lane >> 1) & 7;
-    c.kh = c.lane >> 5;
+    c.kh = c.lane >> 4;
     return c;
 }
 
@@ -173,14 +180,14 @@ __device__ __forceinline__ void dma16(const char *src, uint16_t *dst)
 // acc += X[m0 .. m0+BM-1, k] . Wt^T over k-tiles [kt0, kt1), where the 256
 // rows of the W tile Wt are W[n0 .. n0+255] or, GATED, 32-row blocks taken in
 // turn from the gate half W[0 .. N) and the up half W[N .. 2N) of a packed
-// [gate; up] weight: tile row 64 q + 32 h + i is W[h N + n0 + 32 q + i], so a
-// wave's two 32-column MFMA blocks hold the gate and the up projection of the
-// same 32 output columns n0 + 32 q + [0, 32).  Rows past the end are clamped
+// [gate; up] weight: tile row 64 q + 32 h + i is W[h N + n0 + 32 q + i], so
+// wave q's 16-column MFMA blocks 0, 1 hold the gate and blocks 2, 3 the up
+// projection of the same 32 output columns n0 + 32 q + [0, 32).  Rows past the end are clamped
 // (computed and discarded).  Starts with a barrier, so the LDS may still be in
 // use by the caller's previous tile when it is called.
 template <int TM, bool GATED>
 __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, const Ctx &c, int m0, int n0,
-                                         int kt0, int kt1, f32x16 (&acc)[TM][TN])
+                                         int kt0, int kt1, f32x4 (&acc)[Tile<TM>::XB][WB])
 {
     // Per-lane byte offsets (32-bit: operands are below 2 GiB) from
     // wave-uniform bases, so the DMA uses the scalar-base addressing form.
@@ -215,32 +222,31 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
     auto read_frags = [&](int stage, int s, Frags<TM> &f) {
         const uint16_t *xs = lds + stage * L::kStageElems;
         const uint16_t *ws = xs + L::kXElems;
-        const int cpos = ((s * 2 + c.kh) ^ c.swz) * 8;
+        const int cpos = ((s * 4 + c.kh) ^ c.swz) * 8;
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-            f.x[i] = *reinterpret_cast<const bf16x8 *>(xs + c.xrow_off + i * 32 * BK + cpos);
+        for (int i = 0; i < L::XB; ++i)
+            f.x[i] = *reinterpret_cast<const bf16x8 *>(xs + c.xrow_off + i * 16 * BK + cpos);
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-            f.w[j] = *reinterpret_cast<const bf16x8 *>(ws + c.wrow_off + j * 32 * BK + cpos);
+        for (int j = 0; j < WB; ++j)
+            f.w[j] = *reinterpret_cast<const bf16x8 *>(ws + c.wrow_off + j * 16 * BK + cpos);
     };
     auto mma = [&](const Frags<TM> &f) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < L::XB; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[j], f.x[i], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < WB; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.w[j], f.x[i], acc[i][j], 0, 0, 0);
     };
-    // Pipeline: stage t % 2 holds k-tile t; steps s = 0..3 are its k16 slices.
+    // Pipeline: stage t % 2 holds k-tile t; steps s = 0, 1 are its k32 slices.
     // TPL_STEP(read next, mma current) fixes the order of one step for the
-    // scheduler: MFMA, 2 reads, MFMA, 2 reads, MFMA, 2 reads, 5 MFMAs.
-#define TPL_STEP(RD, MM) do { RD; MM;                                    \
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                \
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                \
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                \
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                \
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                \
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                \
-        __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);                \
+    // scheduler: (MFMA, read) for each of the next step's fragments, then the
+    // remaining MFMAs.
+#define TPL_STEP(RD, MM) do { RD; MM;                                        \
+        _Pragma("unroll") for (int g_ = 0; g_ < L::XB + WB; ++g_) {           \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                \
+        }                                                                     \
+        __builtin_amdgcn_sched_group_barrier(0x008, L::XB * WB - (L::XB + WB), 0); \
         __builtin_amdgcn_sched_barrier(0); } while (0)
     const int T = kt1 - kt0;
     Frags<TM> f0, f1;
@@ -253,16 +259,12 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
     for (int t = 0; t < T - 1; ++t) {
         const int st = t & 1;
         TPL_STEP(read_frags(st, 1, f1), mma(f0));
-        TPL_STEP(read_frags(st, 2, f0), mma(f1));
-        TPL_STEP(read_frags(st, 3, f1), mma(f0));
         __syncthreads();
         if (t + 2 < T)
             issue(st, (t + 2) * BK);
         TPL_STEP(read_frags(st ^ 1, 0, f0), mma(f1));
     }
     TPL_STEP(read_frags((T - 1) & 1, 1, f1), mma(f0));
-    TPL_STEP(read_frags((T - 1) & 1, 2, f0), mma(f1));
-    TPL_STEP(read_frags((T - 1) & 1, 3, f1), mma(f0));
     mma(f1);
 #undef TPL_STEP
 }
@@ -277,78 +279,69 @@ constexpr int kActGelu = 1;
 constexpr int kActSwiglu = 2;  // W tile = interleaved [gate; up] 32-row blocks, see mainloop
 
 // Epilogue through LDS.  Lane l holds Y[m][n..n+3] for m = row base +
-// 32 i + l%32 and n = column base + 32 j + 8 q + 4 (l / 32).  For each of
-// the wave's 32-row slices the wave writes its output values (after bias /
+// 16 i + l%16 and n = column base + 16 j + 4 (l / 16).  For each of the
+// wave's 16-row slices the wave writes its output values (after bias /
 // activation / rounding) into a private LDS area with padded rows, then
 // reads them back row-major and stores whole row segments.  A wave owns 64
-// output columns, or 32 with SwiGLU: there its block j = 0 holds the gate and
-// j = 1 the up projection of the same 32 columns, and the output is
+// output columns, or 32 with SwiGLU: there its blocks j = 0, 1 hold the gate
+// and j = 2, 3 the up projection of the same 32 columns, and the output is
 // silu(gate + b_gate) * (up + b_up), the bias being [b_gate; b_up] (2 N).
 template <int TM, bool OUT_BF16, bool HAS_BIAS, int ACT>
 __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, const Ctx &c, int m0, int n0,
-                                         const f32x16 (&acc)[TM][TN])
+                                         const f32x4 (&acc)[Tile<TM>::XB][WB])
 {
     __syncthreads();  // every wave is done reading the operand stages
     typedef typename std::conditional<OUT_BF16, __bf16, float>::type OutT;
     constexpr bool kGated = ACT == kActSwiglu;
-    constexpr int WNO = kGated ? 32 : WN;   // output columns per wave
-    constexpr int JO = kGated ? 1 : TN;     // output column blocks per wave
+    constexpr int WNO = kGated ? WN / 2 : WN;  // output columns per wave
+    constexpr int JO = WNO / 16;               // 16-column output blocks per wave
     constexpr int kOutEs = sizeof(OutT);
     constexpr int kRowElems = WNO + 16 / kOutEs;  // one 16-byte pad per row
-    OutT *stage = reinterpret_cast<OutT *>(lds) + c.wave * 32 * kRowElems;
-    const int mrow = c.lane & 31;
-    const int ncol = 4 * (c.lane >> 5);
-    f32x4 bj[TN][4];
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            bj[j][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int n = kGated ? n0 + c.wave_n * WNO + q * 8 + ncol : n0 + c.wave_n * WN + j * 32 + q * 8 + ncol;
-            if (HAS_BIAS && n < p.N) {
-                const bf16x4 bb = *reinterpret_cast<const bf16x4 *>(p.bias + (kGated ? j * p.N + n : n));
-                bj[j][q] = f32x4{(float)bb[0], (float)bb[1], (float)bb[2], (float)bb[3]};
-            }
-        }
+    OutT *stage = reinterpret_cast<OutT *>(lds) + c.wave * 16 * kRowElems;
+    const int mrow = c.lane & 15;
+    const int ncol = 4 * (c.lane >> 4);
+    auto bias4 = [&](int e) {
+        const bf16x4 bb = *reinterpret_cast<const bf16x4 *>(p.bias + e);
+        return f32x4{(float)bb[0], (float)bb[1], (float)bb[2], (float)bb[3]};
+    };
     constexpr int kVec = 16 / kOutEs;              // elements per 16-byte vector
     constexpr int kVecPerRow = WNO / kVec;
     constexpr int kRowsPerPass = 64 / kVecPerRow;
     const int rd_row = c.lane / kVecPerRow;
     const int rd_vec = c.lane % kVecPerRow;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < Tile<TM>::XB; ++i) {
 #pragma unroll
-        for (int j = 0; j < JO; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                f32x4 v = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                if (HAS_BIAS)
-                    v = v + bj[j][q];
-                if (ACT == kActGelu) {
-                    v[0] = gelu_tanh(v[0]);
-                    v[1] = gelu_tanh(v[1]);
-                    v[2] = gelu_tanh(v[2]);
-                    v[3] = gelu_tanh(v[3]);
-                }
-                if (kGated) {
-                    f32x4 u = f32x4{acc[i][1][4 * q], acc[i][1][4 * q + 1], acc[i][1][4 * q + 2], acc[i][1][4 * q + 3]};
-                    if (HAS_BIAS)
-                        u = u + bj[1][q];
-                    v[0] = silu(v[0]) * u[0];
-                    v[1] = silu(v[1]) * u[1];
-                    v[2] = silu(v[2]) * u[2];
-                    v[3] = silu(v[3]) * u[3];
-                }
-                OutT *dst = stage + mrow * kRowElems + j * 32 + q * 8 + ncol;
-                if (OUT_BF16)
-                    *reinterpret_cast<bf16x4 *>(dst) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-                else
-                    *reinterpret_cast<f32x4 *>(dst) = v;
+        for (int j = 0; j < JO; ++j) {
+            const int n = n0 + c.wave_n * WNO + j * 16 + ncol;  // N % 16 == 0: n < N covers n + 3
+            f32x4 v = acc[i][j];
+            if (HAS_BIAS && n < p.N)
+                v = v + bias4(n);
+            if (ACT == kActGelu) {
+                v[0] = gelu_tanh(v[0]);
+                v[1] = gelu_tanh(v[1]);
+                v[2] = gelu_tanh(v[2]);
+                v[3] = gelu_tanh(v[3]);
             }
-        const int mbase = m0 + c.wave_m * Tile<TM>::WM + i * 32;
+            if (kGated) {
+                f32x4 u = acc[i][j + 2];
+                if (HAS_BIAS && n < p.N)
+                    u = u + bias4(p.N + n);
+                v[0] = silu(v[0]) * u[0];
+                v[1] = silu(v[1]) * u[1];
+                v[2] = silu(v[2]) * u[2];
+                v[3] = silu(v[3]) * u[3];
+            }
+            OutT *dst = stage + mrow * kRowElems + j * 16 + ncol;
+            if (OUT_BF16)
+                *reinterpret_cast<bf16x4 *>(dst) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+            else
+                *reinterpret_cast<f32x4 *>(dst) = v;
+        }
+        const int mbase = m0 + c.wave_m * Tile<TM>::WM + i * 16;
         const int ncol0 = n0 + c.wave_n * WNO + rd_vec * kVec;
 #pragma unroll
-        for (int r = 0; r < 32; r += kRowsPerPass) {
+        for (int r = 0; r < 16; r += kRowsPerPass) {
             const int row = r + rd_row;
             const int m = mbase + row;
             const f32x4 v = *reinterpret_cast<const f32x4 *>(stage + row * kRowElems + rd_vec * kVec);
@@ -359,15 +352,13 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, con
 }
 
 template <int TM>
-__device__ __forceinline__ void zero(f32x16 (&acc)[TM][TN])
+__device__ __forceinline__ void zero(f32x4 (&acc)[Tile<TM>::XB][WB])
 {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < Tile<TM>::XB; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                acc[i][j][e] = 0.f;
+        for (int j = 0; j < WB; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // One BM x 256 output tile per workgroup (BM x 128 output columns with
@@ -383,7 +374,7 @@ void gemm_bf16_nt_kernel(GemmParams p)
     const Ctx c = make_ctx<TM>();
     int tm, tn;
     tile_of(xcd_contiguous(blockIdx.x, p.tiles_m * p.tiles_n), p, tm, tn);
-    f32x16 acc[TM][TN];
+    f32x4 acc[Tile<TM>::XB][WB];
     zero<TM>(acc);
     mainloop<TM, kGated>(p, lds, c, tm * BM, tn * kTileCols, 0, p.K / BK, acc);
     epilogue<TM, OUT_BF16, HAS_BIAS, ACT>(p, lds, c, tm * BM, tn * kTileCols, acc);
