@@ -54,7 +54,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
-    ap.add_argument("--detail", action="store_true", help="also print a per-shape GEMM table to stderr")
+    ap.add_argument("--detail", action="store_true", help="time every launch with its own event pair (adds the events' overhead to the step) "
+                         "and print a per-shape table to stderr")
     ap.add_argument("--streams", type=int, default=1, choices=(1, 2),
                     help="2: slicing and combines on a second stream beside the GEMMs (measured slower)")
     ap.add_argument("--probe", metavar="OUT_JSON",
@@ -146,12 +147,27 @@ def reduce_traffic(fetch_dir, write_dir, probe_json):
 
 
 class Timer:
-    """HIP events around launches on torch's current stream (the library's stream)."""
+    """HIP events over the timed launches, on the stream each launch runs on.
 
-    def __init__(self, torch):
+    By default consecutive launches of one kernel family on one stream share
+    one event pair, so the events add no gaps between them; a family's
+    average launch time is the summed group time over its launch count.
+    With per_launch=True every launch gets its own pair (per-shape detail).
+    """
+
+    def __init__(self, torch, per_launch=False):
         self.torch = torch
         self.on = False
-        self.rec = []  # (category, key, work, bytes, ev0, ev1)
+        self.per_launch = per_launch
+        self.rec = []    # (category, [(key, flops, bytes), ...], ev0, ev1)
+        self.open = {}   # stream -> [category, items, ev0]
+
+    def _close(self, s):
+        g = self.open.pop(s, None)
+        if g is not None:
+            e1 = self.torch.cuda.Event(enable_timing=True)
+            e1.record(s)
+            self.rec.append((g[0], g[1], g[2], e1))
 
     def run(self, cat, key, flops, nbytes, fn, stream=None):
         """Launch fn on `stream` (torch's current stream if None), timed by events on it."""
@@ -159,29 +175,42 @@ class Timer:
         with self.torch.cuda.stream(s):
             if not self.on:
                 return fn()
-            e0 = self.torch.cuda.Event(enable_timing=True)
-            e1 = self.torch.cuda.Event(enable_timing=True)
-            e0.record(s)
+            g = self.open.get(s)
+            if self.per_launch or g is None or g[0] != cat:
+                self._close(s)
+                e0 = self.torch.cuda.Event(enable_timing=True)
+                e0.record(s)
+                g = self.open[s] = [cat, [], e0]
             out = fn()
-            e1.record(s)
-        self.rec.append((cat, key, flops, nbytes, e0, e1))
+            g[1].append((key, flops, nbytes))
+            if self.per_launch:
+                self._close(s)
         return out
+
+    def flush(self):
+        """Close the open groups (end of a step)."""
+        for s in list(self.open):
+            with self.torch.cuda.stream(s):
+                self._close(s)
 
     def summary(self):
         cats = {}
         shapes = {}
-        for cat, key, flops, nbytes, e0, e1 in self.rec:
+        for cat, items, e0, e1 in self.rec:
             ms = e0.elapsed_time(e1)
             c = cats.setdefault(cat, dict(ms=0.0, flops=0.0, bytes=0.0, launches=0))
             c["ms"] += ms
-            c["flops"] += flops
-            c["bytes"] += nbytes
-            c["launches"] += 1
-            s = shapes.setdefault(f"{cat}: {key}", dict(ms=0.0, flops=0.0, bytes=0.0, launches=0))
-            s["ms"] += ms
-            s["flops"] += flops
-            s["bytes"] += nbytes
-            s["launches"] += 1
+            c["launches"] += len(items)
+            for key, flops, nbytes in items:
+                c["flops"] += flops
+                c["bytes"] += nbytes
+            if len(items) == 1:
+                key, flops, nbytes = items[0]
+                sh = shapes.setdefault(f"{cat}: {key}", dict(ms=0.0, flops=0.0, bytes=0.0, launches=0))
+                sh["ms"] += ms
+                sh["flops"] += flops
+                sh["bytes"] += nbytes
+                sh["launches"] += 1
         return cats, shapes
 
 
@@ -270,7 +299,7 @@ def main():
     gen = torch.Generator(device="cpu").manual_seed(5)
     b_ada = torch.randn(n_full_ada, generator=gen).to(torch.bfloat16).to(dev)
 
-    T = Timer(torch)
+    T = Timer(torch, per_launch=args.detail)
     gemm_flops_step = 0.0
 
     def gemm_cost(m_, n_, k_, out_es):
@@ -381,6 +410,7 @@ def main():
             mark(ms, ("adas read", r))
         T.run("sum", f"adaLN P{P_ADA} bf16", 0, (P_ADA * 4.0 + 2.0) * B_ADA * n_full_ada + 2.0 * n_full_ada,
               lambda: tsl.tp_partial_combine(ada_p, "sum", bias=b_ada, out=ada_sum), ms)
+        T.flush()
 
     for P in tps:
         gemm_flops_step += P * 2.0 * M * hidden * (3 * H // P * hd + ffn // P) + \
@@ -396,12 +426,12 @@ def main():
         step()
         torch.cuda.synchronize()
         T.on = False
-        g = [r for r in T.rec if r[0] == "gemm"]
+        g = [it for r in T.rec if r[0] == "gemm" for it in r[1]]
         cal = torch.empty(CAL_ROWS, CAL_COLS, dtype=torch.bfloat16, device=dev)
         tsl.tp_plan_shard_slice(cal, None, "colwise", 1, 0)
         torch.cuda.synchronize()
         with open(args.probe, "w") as f:
-            json.dump(dict(gemm_launches_per_step=len(g), alg_bytes_per_launch=sum(r[3] for r in g) / len(g),
+            json.dump(dict(gemm_launches_per_step=len(g), alg_bytes_per_launch=sum(it[2] for it in g) / len(g),
                            cal_bytes=2 * CAL_ROWS * CAL_COLS), f)
         print(f"probe: {len(g)} GEMM launches per step", flush=True)
         return
