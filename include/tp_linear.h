@@ -6,8 +6,9 @@
  * Source pages (Hugging Face Diffusers documentation):
  *   [TP] "Tensor parallelism": the opening definition (weights split by
  *        column or row, partial results joined by AllReduce / AllGather at the
- *        layer boundary), "Colwise and rowwise", "Fused projections",
- *        "What to leave out", "Constraints and verification".
+ *        layer boundary), "Load a sharded model", "Limitations", "Colwise and
+ *        rowwise", "Fused projections", "What to leave out", "Constraints and
+ *        verification".
  *   [DI] "Distributed inference": section "Tensor parallelism".
  *
  * Conventions shared by every entry point
@@ -18,16 +19,19 @@
  *           consecutive rows.
  * Dtypes.   Weights, activations and biases are bf16 (16-bit brain float,
  *           passed as raw bits).  Rowwise partial sums are fp32.
- * Pointers. Every pointer argument except `parts` and `blocks` (host arrays)
- *           is a DEVICE pointer on the current HIP device.  The caller owns
+ * Pointers. Every pointer argument except `parts` and `blocks` (host arrays),
+ *           the shape / dtype outputs and tp_load_shard's `path` and `name`
+ *           (host strings) is a DEVICE pointer on the current HIP device.  The caller owns
  *           all memory; the library allocates no device memory and keeps no
  *           state between calls apart from the thread-local error message.
  * Streams.  Work is enqueued on `stream` (0 = the legacy default stream) and
  *           TP_OK means "enqueued": synchronise the stream before reading the
- *           results on the host.
+ *           results on the host.  tp_load_shard alone returns after its
+ *           copies have completed.
  * Errors.   Arguments are checked before any HIP call.  On a non-OK status
- *           nothing has been launched or written, and tp_last_error() returns
- *           a message for the calling thread.  There is no fallback path: an
+ *           nothing has been launched or written (tp_load_shard: a read error
+ *           found part-way may leave the destination partly written), and
+ *           tp_last_error() returns a message for the calling thread.  There is no fallback path: an
  *           unsupported request is an error.
  * Alignment. Device base pointers must be 16-byte aligned and every ld a
  *           multiple of 16 bytes (8 bf16 / 4 fp32 elements) unless stated
@@ -51,7 +55,8 @@ typedef enum {
     TP_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad ld, rank, dtype, mode ...  */
     TP_ERR_NOT_DIVISIBLE = -2, /* a divisibility rule of the plan is violated             */
     TP_ERR_UNSUPPORTED = -3,   /* valid request outside what the kernels implement        */
-    TP_ERR_HIP = -4            /* the HIP runtime reported an error at launch             */
+    TP_ERR_HIP = -4,           /* the HIP runtime reported an error at launch             */
+    TP_ERR_IO = -5             /* a checkpoint file could not be read or is malformed     */
 } tp_status;
 
 typedef enum { TP_BF16 = 0, TP_F32 = 1 } tp_dtype;
@@ -234,6 +239,43 @@ tp_status tp_plan_shard_slice(const void *w_full, const void *b_full, void *w_sh
                               tp_dtype dtype, tp_style style, const int64_t *blocks,
                               int num_blocks, int tp_degree, int rank, int64_t *shard_rows,
                               int64_t *shard_cols, hipStream_t stream);
+
+/*
+ * tp_load_shard -- [TP] "Load a sharded model" (the checkpoint is sharded as it
+ * is read: each rank reads only its own slice of each weight and places it on
+ * its GPU, so no rank holds a full-size weight) and "Limitations" (the sharded
+ * load works with safetensors weights only).  Reads rank `rank`'s shard of
+ * the tensor `name` of the safetensors file `path` into device memory.
+ *
+ *   path, name host strings, read during the call.
+ *   A 2-D tensor [out, in] is cut like tp_plan_shard_slice cuts it (style,
+ *   blocks, tp_degree, rank; same rules and errors).  A 1-D tensor (a bias) is
+ *   cut like the rows of a colwise weight, blocks included, and only with
+ *   TP_COLWISE (a rowwise bias is not sharded: load it whole with tp_degree 1).
+ *   dst        device buffer of dst_bytes >= the shard's bytes, owned by the
+ *              caller; the shard is written row-major and contiguous
+ *              (ld = shard_cols).  NULL: query only -- reads the header, fills
+ *              the outputs, makes no HIP call.
+ *   shard_rows, shard_cols, dtype   host outputs (each may be NULL); a 1-D
+ *              shard reports shard_rows = 1.
+ *
+ * Only the byte ranges of the rank's slice are read (one range per packed
+ * block for a colwise cut, one range per row and block for a rowwise cut),
+ * through two pinned host staging buffers of at most 32 MiB each, allocated
+ * and freed inside the call, with the host-to-device copy of one buffer on
+ * `stream` overlapping the read into the other: the host memory used is the
+ * header plus those buffers, whatever the tensor's size.  The call returns
+ * when the shard is on the device.  Tensor dtypes BF16 and F32 are supported.
+ * Errors: TP_ERR_IO (file missing or unreadable, malformed header, tensor
+ * absent, data range outside the file, a failed read), TP_ERR_UNSUPPORTED
+ * (other dtypes, other than one or two dimensions, a dimension of 0 or above
+ * 2^30), TP_ERR_INVALID_ARG / TP_ERR_NOT_DIVISIBLE as for tp_plan_shard_slice,
+ * TP_ERR_INVALID_ARG for a rowwise cut of a 1-D tensor or a dst_bytes below
+ * the shard's size, TP_ERR_HIP for runtime failures.
+ */
+tp_status tp_load_shard(const char *path, const char *name, tp_style style, const int64_t *blocks,
+                        int num_blocks, int tp_degree, int rank, void *dst, int64_t dst_bytes,
+                        int64_t *shard_rows, int64_t *shard_cols, tp_dtype *dtype, hipStream_t stream);
 
 /* Message describing the last non-OK status returned on the calling thread
  * (empty string if none).  The pointer stays valid until the next call on

@@ -279,6 +279,62 @@ def qkv_split(w, b, num_heads: int, head_dim: int, tp_degree: int, rank: int):
 
 
 # --------------------------------------------------------------------------------------
+# Checkpoint reading
+# --------------------------------------------------------------------------------------
+
+_ST_DTYPES = {"BF16": np.dtype("<u2"), "F32": np.dtype("<f4")}
+
+
+def read_safetensors(path: str, name: str):
+    """[TP] "Load a sharded model" / "Limitations": the sharded load reads safetensors
+    files.  Tensor ``name`` read whole, from the format's published definition: an 8-byte
+    little-endian header length H, H bytes of JSON mapping each name to its dtype, shape and
+    ``data_offsets`` [begin, end) into the byte buffer that follows the header, and row-major
+    data.  Returns ``(array, dtype_name)``; BF16 comes back as uint16 bit patterns."""
+    import json
+    with open(path, "rb") as f:
+        h = int.from_bytes(f.read(8), "little")
+        header = json.loads(f.read(h).decode("utf-8"))
+        entry = header[name]
+        begin, end = entry["data_offsets"]
+        f.seek(8 + h + begin)
+        raw = f.read(end - begin)
+    dt = _ST_DTYPES[entry["dtype"]]
+    shape = tuple(entry["shape"])
+    if len(raw) != int(np.prod(shape)) * dt.itemsize:
+        raise ValueError("data_offsets do not match the shape")
+    return np.frombuffer(raw, dtype=dt).reshape(shape).astype(dt.newbyteorder("="), copy=True), entry["dtype"]
+
+
+def load_shard(path: str, name: str, style: str, tp_degree: int, rank: int, blocks=None):
+    """[TP] "Load a sharded model": rank ``rank``'s shard of tensor ``name`` -- the whole
+    tensor read by :func:`read_safetensors`, then cut by this module's slicers (a colwise cut
+    of a 1-D bias takes its rows; a rowwise cut takes the columns of W, i.e. the rows of
+    W^T, so packed rowwise blocks reuse the packed colwise slicer on W^T).  fp32 tensors are
+    sliced as pairs of uint16 halves, which leaves every cut bit-exact."""
+    t, dt = read_safetensors(path, name)
+    u = t.view(np.uint16) if dt == "F32" else t   # [.., 2 * cols] for fp32
+    per = 2 if dt == "F32" else 1
+    if t.ndim == 1:
+        if style != "colwise":
+            raise PlanError("a 1-D tensor is sharded colwise only")
+        col = u.reshape(t.shape[0], per)
+        ws = shard_packed_colwise(col, None, blocks or [1], tp_degree, rank)[0]
+        out = ws.reshape(-1)
+    elif style == "colwise":
+        out = shard_packed_colwise(u, None, blocks or [1], tp_degree, rank)[0]
+    elif style in ("rowwise", "rowwise_split_input"):
+        n, k = t.shape
+        # columns of W (in units of whole elements): slice W^T's rows, then transpose back
+        wt = np.ascontiguousarray(u.reshape(n, k, per).transpose(1, 0, 2).reshape(k, n * per))
+        s_t = shard_packed_colwise(wt, None, blocks or [1], tp_degree, rank)[0]
+        out = np.ascontiguousarray(s_t.reshape(k // tp_degree, n, per).transpose(1, 0, 2).reshape(n, -1))
+    else:
+        raise ValueError("style must be colwise, rowwise or rowwise_split_input")
+    return (out.view(np.float32) if dt == "F32" else out), dt
+
+
+# --------------------------------------------------------------------------------------
 # Combine
 # --------------------------------------------------------------------------------------
 

@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     SIGNATURES,
     TPError,
+    TPIOError,
     TPRuntimeError,
     TPValueError,
     load_library,
@@ -18,6 +19,8 @@ from ._binding import (  # noqa: F401
     tp_linear_colwise,
     tp_linear_rowwise,
     tp_linear_rowwise_split_input,
+    tp_load_shard,
+    tp_load_shard_shape,
     tp_partial_combine,
     tp_plan_shard_shape,
     tp_plan_shard_slice,
@@ -25,6 +28,6 @@ from ._binding import (  # noqa: F401
 
 __all__ = [
     "tp_linear_colwise", "tp_linear_rowwise", "tp_linear_rowwise_split_input", "tp_fused_qkv_split", "tp_partial_combine",
-    "tp_plan_shard_slice", "tp_plan_shard_shape", "tp_last_error", "load_library", "TPError",
-    "TPValueError", "TPRuntimeError",
+    "tp_plan_shard_slice", "tp_plan_shard_shape", "tp_load_shard", "tp_load_shard_shape", "tp_last_error",
+    "load_library", "TPError", "TPValueError", "TPRuntimeError", "TPIOError",
 ]

@@ -22,6 +22,7 @@ TP_ERR_INVALID_ARG = -1
 TP_ERR_NOT_DIVISIBLE = -2
 TP_ERR_UNSUPPORTED = -3
 TP_ERR_HIP = -4
+TP_ERR_IO = -5
 
 TP_BF16 = 0
 TP_F32 = 1
@@ -47,6 +48,8 @@ SIGNATURES = {
                                 ctypes.POINTER(_I64), _I, _I64, _I64, _P]),
     "tp_plan_shard_slice": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _I, ctypes.POINTER(_I64), _I, _I,
                                  _I, ctypes.POINTER(_I64), ctypes.POINTER(_I64), _P]),
+    "tp_load_shard": (_I, [ctypes.c_char_p, ctypes.c_char_p, _I, ctypes.POINTER(_I64), _I, _I, _I, _P, _I64,
+                           ctypes.POINTER(_I64), ctypes.POINTER(_I64), ctypes.POINTER(_I), _P]),
     "tp_last_error": (ctypes.c_char_p, []),
 }
 
@@ -67,6 +70,10 @@ class TPValueError(TPError, ValueError):
 
 class TPRuntimeError(TPError, RuntimeError):
     """The HIP runtime reported an error."""
+
+
+class TPIOError(TPError, OSError):
+    """A checkpoint file could not be read or is malformed."""
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -98,6 +105,8 @@ def _check(status: int) -> None:
     msg = tp_last_error()
     if status == TP_ERR_HIP:
         raise TPRuntimeError(status, msg)
+    if status == TP_ERR_IO:
+        raise TPIOError(status, msg)
     raise TPValueError(status, msg)
 
 
@@ -346,3 +355,64 @@ def tp_plan_shard_slice(w_full: torch.Tensor, b_full: Optional[torch.Tensor], st
                                    _DT[w_full.dtype], _style(style), bl, nb, tp_degree, rank,
                                    ctypes.byref(r_), ctypes.byref(c_), _stream(stream, w_full)))
     return w_out, b_out
+
+
+_DT_OF = {TP_BF16: torch.bfloat16, TP_F32: torch.float32}
+
+
+def tp_load_shard_shape(path: str, name: str, style: str = "colwise", tp_degree: int = 1, rank: int = 0, *,
+                        blocks: Optional[Sequence[int]] = None):
+    """Shape query of :func:`tp_load_shard`: reads the file's header only.
+
+    Returns ``(shard_rows, shard_cols, dtype)``; a 1-D tensor reports one row."""
+    lib = load_library()
+    rows, cols, dt = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int(0)
+    bl, nb = _blocks(blocks)
+    _check(lib.tp_load_shard(os.fsencode(path), name.encode(), _style(style), bl, nb, tp_degree, rank, None, 0,
+                             ctypes.byref(rows), ctypes.byref(cols), ctypes.byref(dt), None))
+    return rows.value, cols.value, _DT_OF[dt.value]
+
+
+def tp_load_shard(path: str, name: str, style: str = "colwise", tp_degree: int = 1, rank: int = 0, *,
+                  blocks: Optional[Sequence[int]] = None, out: Optional[torch.Tensor] = None,
+                  device=None, stream=None) -> torch.Tensor:
+    """Rank ``rank``'s shard of tensor ``name`` read from the safetensors file ``path``
+    straight into GPU memory (only the slice's bytes are read).
+
+    A 2-D weight is cut by ``style`` (and packed ``blocks``) like
+    :func:`tp_plan_shard_slice`; a 1-D bias only colwise.  Returns a contiguous
+    GPU tensor of the file's dtype: ``[rows, cols]``, or ``[cols]`` for a bias."""
+    lib = load_library()
+    rows, cols, dt = tp_load_shard_shape(path, name, style, tp_degree, rank, blocks=blocks)
+    one_d = False
+    if out is None:
+        dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        if dev.type != "cuda":
+            raise TypeError("tp_load_shard writes GPU memory (there is no CPU path)")
+        # a 1-D tensor comes back 1-D
+        n_dims = _header_ndim(path, name)
+        one_d = n_dims == 1
+        out = torch.empty((cols,) if one_d else (rows, cols), dtype=dt, device=dev)
+    if not isinstance(out, torch.Tensor) or not out.is_cuda or not out.is_contiguous() or out.dtype != dt:
+        raise ValueError(f"out must be a contiguous {dt} GPU tensor")
+    if out.numel() != rows * cols:
+        raise ValueError(f"out must hold {rows} x {cols} elements, got shape {tuple(out.shape)}")
+    bl, nb = _blocks(blocks)
+    r_, c_, d_ = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int(0)
+    _check(lib.tp_load_shard(os.fsencode(path), name.encode(), _style(style), bl, nb, tp_degree, rank,
+                             out.data_ptr(), out.numel() * out.element_size(), ctypes.byref(r_), ctypes.byref(c_),
+                             ctypes.byref(d_), _stream(stream, out)))
+    return out
+
+
+def _header_ndim(path: str, name: str) -> int:
+    """Rank of tensor ``name``: a 1-D query reports rows == 1 and so does a [1, n] weight;
+    the library's colwise query of tp_degree 1 tells them apart by the row count."""
+    rows, _, _ = tp_load_shard_shape(path, name, "colwise", 1, 0)
+    if rows != 1:
+        return 2
+    try:  # a rowwise cut of a 1-D tensor is rejected, of a [1, n] weight accepted
+        tp_load_shard_shape(path, name, "rowwise", 1, 0)
+        return 2
+    except TPValueError:
+        return 1

@@ -14,7 +14,7 @@
 
 namespace {
 
-thread_local char g_msg[512] = "";
+thread_local char g_msg[tpl::kLastErrorBytes] = "";
 
 tp_status fail(tp_status s, const char *fmt, ...)
 {
@@ -118,6 +118,8 @@ tp_status check_blocks(const char *fn, const int64_t *blocks, int nb, int64_t di
 }
 
 }  // namespace
+
+char *tpl::last_error_buffer() { return g_msg; }
 
 extern "C" {
 

@@ -8,6 +8,10 @@
 
 namespace tpl {
 
+// The calling thread's message for the last non-OK status (tp_last_error()).
+constexpr int kLastErrorBytes = 512;
+char *last_error_buffer();
+
 // Problem description of one linear-layer launch: Y = epilogue(X . W^T).
 // X [M, K] bf16 (row stride ldx), W [N, K] bf16 (row stride ldw), Y [M, N]
 // (row stride ldy) in bf16 or fp32, optional bias [N] bf16, optional GELU-tanh.

@@ -32,7 +32,8 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = tsl.load_library()
     syms = declared_symbols()
     assert syms == {"tp_linear_colwise", "tp_linear_rowwise", "tp_linear_rowwise_split_input",
-                    "tp_fused_qkv_split", "tp_partial_combine", "tp_plan_shard_slice", "tp_last_error"}
+                    "tp_fused_qkv_split", "tp_partial_combine", "tp_plan_shard_slice", "tp_load_shard",
+                    "tp_last_error"}
     for s in syms:
         assert hasattr(lib, s), s
     assert set(B.SIGNATURES) == syms
