@@ -63,7 +63,193 @@ def parse():
                          "FETCH_SIZE / WRITE_SIZE runs; writes the step's algorithmic GEMM bytes to OUT_JSON")
     ap.add_argument("--traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PROBE_JSON"),
                     help="no GPU: reduce the two counter runs of --probe to " + os.path.relpath(TRAFFIC_FILE, ROOT))
+    ap.add_argument("--load", action="store_true",
+                    help="checkpoint-load benchmark instead of the step: the full block's weights in a synthetic "
+                         "safetensors file, every rank of --load-tp loaded by tp_load_shard (shard as read) and "
+                         "by reading whole tensors then slicing on the device; time and peak host memory")
+    ap.add_argument("--load-tp", type=int, default=4)
+    ap.add_argument("--load-dir", default=None, help="directory for the synthetic checkpoint (default: a temp dir)")
+    ap.add_argument("--load-child", nargs=4, metavar=("METHOD", "TP", "PATH", "OUT_JSON"), help=argparse.SUPPRESS)
     return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------------------------
+# checkpoint-load benchmark ("Load a sharded model" / "Loading performance" of the TP page)
+# ---------------------------------------------------------------------------------------------
+
+# The full block's weights and the plan each is loaded with: (name, style, blocks).
+LOAD_PLAN = [("attn.to_qkv.weight", "colwise", [1, 1, 1]), ("attn.to_out.weight", "rowwise", None),
+             ("ff.w1.weight", "colwise", None), ("ff.w2.weight", "rowwise", None)]
+LOAD_SRC = {"attn.to_qkv.weight": "w_qkv", "attn.to_out.weight": "w_o", "ff.w1.weight": "w1", "ff.w2.weight": "w2"}
+
+
+def _evict(path):
+    """Drop the file's clean pages from the page cache (posix_fadvise, no privileges
+    needed), so the next read comes from the storage device."""
+    fd = os.open(path, os.O_RDONLY)
+    try:
+        os.fsync(fd)
+        os.posix_fadvise(fd, 0, 0, os.POSIX_FADV_DONTNEED)
+    finally:
+        os.close(fd)
+
+
+def _fs_type(path):
+    best, fs = "", "?"
+    with open("/proc/mounts") as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) >= 3 and os.path.realpath(path).startswith(parts[1]) and len(parts[1]) > len(best):
+                best, fs = parts[1], parts[2]
+    return fs
+
+
+def _rss_now_bytes():
+    with open("/proc/self/statm") as f:
+        return int(f.read().split()[1]) * os.sysconf("SC_PAGE_SIZE")
+
+
+class _RssPeak:
+    """Highest resident set size seen while active (sampled every millisecond)."""
+
+    def __init__(self):
+        import threading
+        self.peak = _rss_now_bytes()
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            self.peak = max(self.peak, _rss_now_bytes())
+            self._stop.wait(0.001)
+
+    def __enter__(self):
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join()
+        self.peak = max(self.peak, _rss_now_bytes())
+
+
+def load_child(method, tp, path, out_json):
+    """One process per method: every rank in turn, the file's pages evicted before each.
+    Host memory is the peak resident set during a rank's load above the process's resident
+    set before its first load (so the pinned staging buffers count, even where the runtime
+    keeps them between calls)."""
+    import torch
+    import tensor_sharded_linear_amd as tsl
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    torch.empty(1, device=dev)
+    torch.cuda.synchronize()
+    ranks = []
+    peak_above = 0
+    base_rss = _rss_now_bytes()   # host memory in use before any load (torch and the HIP runtime)
+    for i, r in enumerate([0] + list(range(tp))):
+        warm = i == 0   # an untimed first pass (rank 0) warms up the HIP runtime
+        _evict(path)
+        mon = _RssPeak().__enter__()
+        t0 = time.perf_counter()
+        shard_bytes = 0
+        held = []
+        per = {}
+        if method == "shard":
+            for name, style, blocks in LOAD_PLAN:
+                t1 = time.perf_counter()
+                t = tsl.tp_load_shard(path, name, style, tp, r, blocks=blocks)
+                per[name] = round(time.perf_counter() - t1, 4)
+                shard_bytes += t.numel() * t.element_size()
+                held.append(t)
+        else:
+            from safetensors.torch import load_file
+            full = load_file(path)            # the whole checkpoint in host memory
+            for name, style, blocks in LOAD_PLAN:
+                w = full[name].to(dev)
+                ws, _ = tsl.tp_plan_shard_slice(w, None, style, tp, r, blocks=blocks)
+                shard_bytes += ws.numel() * ws.element_size()
+                held.append(ws)
+                del w
+            del full
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        mon.__exit__()
+        if warm:
+            del held
+            continue
+        ranks.append(dict(rank=r, seconds=round(dt, 4), shard_bytes=shard_bytes,
+                          gbs=round(shard_bytes / dt / 1e9, 3), peak_host_bytes=mon.peak - base_rss))
+        if per:
+            ranks[-1]["seconds_per_tensor"] = per
+        peak_above = max(peak_above, mon.peak - base_rss)
+        del held
+        torch.cuda.empty_cache()
+    with open(out_json, "w") as f:
+        json.dump(dict(method=method, ranks=ranks, peak_host_bytes_above_start=peak_above), f)
+
+
+def load_bench(args):
+    """Parent process: writes the checkpoint (CPU only, never touches the GPU), then runs one
+    child process per method and prints one JSON line."""
+    import subprocess
+    import tempfile
+
+    import numpy as np
+    import torch
+    from safetensors.torch import save_file
+
+    import synth_inputs as si
+
+    d = args.load_dir or tempfile.mkdtemp(prefix="tp_load_", dir="/tmp")
+    path = os.path.join(d, "dit_block_h6144.safetensors")
+    t0 = time.perf_counter()
+    fb = si.workload("full_block").arrays
+    tensors = {n: torch.from_numpy(fb[src].view(np.int16)).view(torch.bfloat16) for n, src in LOAD_SRC.items()}
+    save_file(tensors, path)
+    file_bytes = os.path.getsize(path)
+    del tensors, fb
+    print(f"# checkpoint {path}: {file_bytes / 1e6:.1f} MB written in {time.perf_counter() - t0:.1f}s "
+          f"({_fs_type(path)})", file=sys.stderr, flush=True)
+    def seq_read_gbs():
+        t = time.perf_counter()
+        with open(path, "rb", buffering=0) as f:
+            while f.read(32 << 20):
+                pass
+        return round(file_bytes / (time.perf_counter() - t) / 1e9, 2)
+    _evict(path)
+    cold = seq_read_gbs()
+    warm = seq_read_gbs()
+    print(f"# sequential read of the file: {cold} GB/s after eviction, {warm} GB/s again", file=sys.stderr,
+          flush=True)
+    res = {}
+    for method in ("shard", "full"):
+        out = os.path.join(d, f"{method}.json")
+        cmd = [sys.executable, os.path.abspath(__file__), "--load-child", method, str(args.load_tp), path, out]
+        subprocess.run(cmd, check=True)
+        with open(out) as f:
+            res[method] = json.load(f)
+        print(f"# {method}: {res[method]}", file=sys.stderr, flush=True)
+    if not args.load_dir:
+        os.remove(path)
+    tp = args.load_tp
+
+    def summary(m):
+        rs = res[m]["ranks"]
+        return dict(seconds_per_rank_max=max(r["seconds"] for r in rs),
+                    seconds_per_rank_mean=round(sum(r["seconds"] for r in rs) / len(rs), 4),
+                    shard_gbs_mean=round(sum(r["gbs"] for r in rs) / len(rs), 3),
+                    peak_host_bytes=res[m]["peak_host_bytes_above_start"], ranks=rs)
+    print(json.dumps({
+        "metric": "sharded checkpoint load time per rank (s)", "value": summary("shard")["seconds_per_rank_max"],
+        "unit": "s", "higher_is_better": False, "n_gpus": 1, "data": "synthetic",
+        "config": {"workload": f"DiT block weights (hidden 6144, FFN 18432; W_qkv, W_o, W1, W2 bf16) in one "
+                               f"safetensors file, every rank of tp {tp} loaded in turn on one GPU",
+                   "file_bytes": file_bytes, "tp_degree": tp, "filesystem": _fs_type(path),
+                   "page_cache": "file pages dropped with posix_fadvise(DONTNEED) before each rank",
+                   "sequential_read_gbs": {"after_eviction": cold, "cached": warm}},
+        "shard_as_read": summary("shard"), "full_then_slice": summary("full"),
+    }), flush=True)
 
 
 CAL_ROWS, CAL_COLS = 8192, 8192   # calibration copy: a 128 MiB bf16 weight, copied whole (colwise, P = 1)
@@ -223,6 +409,13 @@ def main():
     args = parse()
     if args.traffic:
         reduce_traffic(*args.traffic)
+        return
+    if args.load_child:
+        m, tp, path, out = args.load_child
+        load_child(m, int(tp), path, out)
+        return
+    if args.load:
+        load_bench(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

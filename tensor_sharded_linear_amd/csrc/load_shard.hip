@@ -26,7 +26,9 @@
 #include <sys/stat.h>
 #include <unistd.h>
 
+#include <algorithm>
 #include <string>
+#include <thread>
 #include <utility>
 #include <vector>
 
@@ -317,6 +319,8 @@ tp_status fail(tp_status s, const char *fmt, ...)
 
 constexpr int64_t kMaxHeaderBytes = (int64_t)100 << 20;  // the header is JSON text: 100 MiB is ample
 constexpr int64_t kStageBytes = (int64_t)32 << 20;       // each of the two pinned staging buffers
+constexpr int kReadThreads = 8;                          // reader threads per staging chunk
+constexpr int64_t kMinBytesPerThread = (int64_t)1 << 20; // below this a chunk is read by fewer threads
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int kMaxBlocks = 16;
 
@@ -430,8 +434,69 @@ void push_run(std::vector<Run> &runs, int64_t file_off, int64_t len, int64_t dst
     runs.push_back(Run{file_off, len, dst_off});
 }
 
+// Reads the pieces of one staging chunk (file offset, length, offset in
+// buf; sorted by that offset, tiling [0, bytes)).  Up to kReadThreads threads
+// take equal shares of the chunk's bytes, so several reads are in flight at
+// once (the strided per-row reads of a rowwise cut would otherwise wait on
+// the storage one at a time).  Returns false and the failing file offset on
+// a read error.
+bool fill_chunk(int fd, char *buf, const std::vector<Run> &pieces, int64_t bytes, int64_t *bad_off)
+{
+    auto read_share = [&](int64_t lo, int64_t hi, int64_t *bad) {
+        // first piece that ends after lo
+        const size_t k0 = (size_t)(std::upper_bound(pieces.begin(), pieces.end(), lo,
+                                                    [](int64_t v, const Run &r) { return v < r.dst_off + r.len; }) -
+                                   pieces.begin());
+        size_t k = k0;
+        // Announce every piece of the share first, so the storage sees them all at once
+        // instead of one read at a time (a hint: errors are ignored).
+        for (size_t j = k0; j < pieces.size() && pieces[j].dst_off < hi && pieces.size() > 1; ++j)
+            (void)posix_fadvise(fd, (off_t)pieces[j].file_off, (off_t)pieces[j].len, POSIX_FADV_WILLNEED);
+        for (; k < pieces.size() && pieces[k].dst_off < hi; ++k) {
+            const Run &p = pieces[k];
+            const int64_t a = p.dst_off > lo ? p.dst_off : lo;
+            const int64_t e = p.dst_off + p.len < hi ? p.dst_off + p.len : hi;
+            if (!read_full(fd, buf + a, e - a, p.file_off + (a - p.dst_off))) {
+                *bad = p.file_off + (a - p.dst_off);
+                return false;
+            }
+        }
+        return true;
+    };
+    int nt = (int)((bytes + kMinBytesPerThread - 1) / kMinBytesPerThread);
+    nt = nt < 1 ? 1 : (nt > kReadThreads ? kReadThreads : nt);
+    if (nt == 1)
+        return read_share(0, bytes, bad_off);
+    std::vector<std::thread> th;
+    std::vector<int64_t> bad((size_t)nt, -1);
+    std::vector<char> ok((size_t)nt, 1);
+    int handed = 1;  // shares 1 .. handed-1 run on their own threads
+    try {
+        for (int t = 1; t < nt; ++t) {
+            th.emplace_back([&, t] { ok[t] = read_share(bytes * t / nt, bytes * (t + 1) / nt, &bad[t]); });
+            handed = t + 1;
+        }
+    } catch (...) {
+        // no more threads: this thread also reads the shares not handed out
+    }
+    bool mine = read_share(0, bytes / nt, &bad[0]);
+    if (mine && handed < nt)
+        mine = read_share(bytes * handed / nt, bytes, &bad[0]);
+    ok[0] = mine;
+    for (auto &x : th)
+        x.join();
+    for (int t = 0; t < nt; ++t)
+        if (!ok[t]) {
+            *bad_off = bad[t];
+            return false;
+        }
+    return true;
+}
+
 // Copies the runs (contiguous in destination order) into dst through two
-// pinned staging buffers; returns when every copy has completed.
+// pinned staging buffers: while the host-to-device copy of one buffer runs on
+// `stream`, the next chunk is read into the other.  Returns when every copy
+// has completed.
 tp_status stream_runs(const char *fn, const char *path, int fd, const std::vector<Run> &runs, int64_t total,
                       char *dst, hipStream_t stream)
 {
@@ -442,10 +507,35 @@ tp_status stream_runs(const char *fn, const char *path, int fd, const std::vecto
     tp_status st = TP_OK;
     hipError_t he = hipSuccess;
     const char *what = "";
-    int cur = 0;
-    int64_t fill = 0;       // bytes staged in stage[cur]
-    int64_t chunk_dst = 0;  // shard offset of stage[cur]'s first byte
 
+    // Cut the runs into staging chunks of at most cap bytes: pieces (file
+    // offset, length, offset in the chunk).
+    std::vector<std::vector<Run>> chunks(1);
+    std::vector<int64_t> chunk_bytes(1, 0);
+    for (const Run &run : runs) {
+        int64_t file_off = run.file_off, len = run.len;
+        while (len > 0) {
+            if (chunk_bytes.back() == cap) {
+                chunks.emplace_back();
+                chunk_bytes.push_back(0);
+            }
+            const int64_t take = len < cap - chunk_bytes.back() ? len : cap - chunk_bytes.back();
+            chunks.back().push_back(Run{file_off, take, chunk_bytes.back()});
+            chunk_bytes.back() += take;
+            file_off += take;
+            len -= take;
+        }
+    }
+    // A chunk of a few large pieces announces the next chunk's ranges before it
+    // is read, so the storage reads ahead across chunks (chunks of many small
+    // pieces announce their own pieces from the reader threads instead).
+    constexpr size_t kPrefetchMaxPieces = 64;
+    auto prefetch = [&](size_t c) {
+        if (c < chunks.size() && chunks[c].size() <= kPrefetchMaxPieces)
+            for (const Run &p : chunks[c])
+                (void)posix_fadvise(fd, (off_t)p.file_off, (off_t)p.len, POSIX_FADV_WILLNEED);
+    };
+    // Allocates staging buffer b on first use, else waits for its last copy.
     auto prepare = [&](int b) -> bool {
         if (!stage[b]) {
             he = hipHostMalloc(&stage[b], (size_t)cap, hipHostMallocDefault);
@@ -471,43 +561,30 @@ tp_status stream_runs(const char *fn, const char *path, int fd, const std::vecto
         }
         return true;
     };
-    auto flush = [&]() -> bool {
-        if (fill == 0)
-            return true;
-        he = hipMemcpyAsync(dst + chunk_dst, stage[cur], (size_t)fill, hipMemcpyHostToDevice, stream);
+
+    int cur = 0;
+    int64_t chunk_dst = 0;  // shard offset of the current chunk's first byte
+    prefetch(0);
+    for (size_t c = 0; c < chunks.size() && chunk_bytes[c] > 0; ++c) {
+        if (!prepare(cur))
+            break;
+        prefetch(c + 1);
+        int64_t bad = 0;
+        if (!fill_chunk(fd, static_cast<char *>(stage[cur]), chunks[c], chunk_bytes[c], &bad)) {
+            st = fail(TP_ERR_IO, "%s: %s: read at offset %lld failed", fn, path, (long long)bad);
+            break;
+        }
+        he = hipMemcpyAsync(dst + chunk_dst, stage[cur], (size_t)chunk_bytes[c], hipMemcpyHostToDevice, stream);
         if (he == hipSuccess)
             he = hipEventRecord(ev[cur], stream);
         if (he != hipSuccess) {
             what = "hipMemcpyAsync";
-            return false;
+            break;
         }
         pending[cur] = true;
-        chunk_dst += fill;
-        fill = 0;
+        chunk_dst += chunk_bytes[c];
         cur ^= 1;
-        return prepare(cur);
-    };
-
-    bool ok = prepare(cur);
-    for (size_t k = 0; ok && k < runs.size(); ++k) {
-        int64_t file_off = runs[k].file_off, len = runs[k].len;
-        while (ok && len > 0) {
-            const int64_t take = len < cap - fill ? len : cap - fill;
-            if (!read_full(fd, static_cast<char *>(stage[cur]) + fill, take, file_off)) {
-                st = fail(TP_ERR_IO, "%s: %s: read of %lld bytes at offset %lld failed", fn, path, (long long)take,
-                          (long long)file_off);
-                ok = false;
-                break;
-            }
-            fill += take;
-            file_off += take;
-            len -= take;
-            if (fill == cap)
-                ok = flush();
-        }
     }
-    if (ok)
-        ok = flush();
     // Every enqueued copy must finish before its staging buffer is freed.
     for (int b = 0; b < 2; ++b) {
         if (pending[b]) {
