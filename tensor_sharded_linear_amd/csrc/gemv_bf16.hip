@@ -1,9 +1,9 @@
-// gemv_bf16.hip -- weight-streaming kernel for skinny linear layers (M <= 16).
+// gemv_bf16.hip -- weight-streaming kernel for skinny linear layers (M <= 8).
 //
 // The adaLN modulation projection reads a handful of conditioning vectors
 // (one per sample) and a large weight; the Diffusers "Tensor parallelism"
 // page (section "What to leave out") singles it out as the one large
-// standalone projection.  With M of 1..16 the work is a matrix-vector product
+// standalone projection.  With M of 1..8 the work is a matrix-vector product
 // bound by how fast the weight streams from HBM, so it gets its own kernel:
 //
 //  * one persistent 512-thread workgroup per CU stages the M activation rows
