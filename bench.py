@@ -523,13 +523,13 @@ def main():
             # shard every weight for every rank (index kernels)
             for r in range(P):
                 wait(cs, ("w read", P, r))
-                T.run("slice", "qkv", 0, 2 * 2 * kq * hidden,
+                T.run("slice", f"qkv P{P}", 0, 2 * 2 * kq * hidden,
                       lambda: tsl.tp_fused_qkv_split(wqkv, None, H, hd, P, r, w_out=b["wq"][r]), cs)
-                T.run("slice", "wo", 0, 2 * 2 * hidden * hidden // P,
+                T.run("slice", f"wo P{P}", 0, 2 * 2 * hidden * hidden // P,
                       lambda: tsl.tp_plan_shard_slice(wo, None, "rowwise", P, r, w_out=b["wo"][r]), cs)
-                T.run("slice", "w1", 0, 2 * 2 * ffn // P * hidden,
+                T.run("slice", f"w1 P{P}", 0, 2 * 2 * ffn // P * hidden,
                       lambda: tsl.tp_plan_shard_slice(w1, None, "colwise", P, r, w_out=b["w1"][r]), cs)
-                T.run("slice", "w2", 0, 2 * 2 * hidden * ffn // P,
+                T.run("slice", f"w2 P{P}", 0, 2 * 2 * hidden * ffn // P,
                       lambda: tsl.tp_plan_shard_slice(w2, None, "rowwise", P, r, w_out=b["w2"][r]), cs)
                 mark(cs, ("w ready", P, r))
             # every rank's projections
@@ -558,9 +558,9 @@ def main():
                   lambda: tsl.tp_partial_combine(b["po"], "sum", out=b["out_sum"]), cs)
             T.run("sum", f"P{P} bf16", 0, (P * 4.0 + 2.0) * M * hidden,
                   lambda: tsl.tp_partial_combine(b["pd"], "sum", out=b["down_sum"]), cs)
-            T.run("concat", "qkv", 0, 2 * 2.0 * M * 3 * H * hd,
+            T.run("concat", f"qkv P{P}", 0, 2 * 2.0 * M * 3 * H * hd,
                   lambda: tsl.tp_partial_combine(b["q"], "concat", blocks=[1, 1, 1], out=b["q_cat"]), cs)
-            T.run("concat", "up", 0, 2 * 2.0 * M * ffn,
+            T.run("concat", f"up P{P}", 0, 2 * 2.0 * M * ffn,
                   lambda: tsl.tp_partial_combine(b["h"], "concat", out=b["h_cat"]), cs)
             mark(cs, ("out read", P))
         # fused gate/up projection with SwiGLU: packed [1, 1] slices, then each rank's GEMM
