@@ -516,41 +516,50 @@ def main():
             e.record(stream)
             ev[key] = e
 
+    def slice_rank(P, r):
+        """Shard every weight for rank r (index kernels)."""
+        b = bufs[P]
+        kq = 3 * H // P * hd
+        wait(cs, ("w read", P, r))
+        T.run("slice", f"qkv P{P}", 0, 2 * 2 * kq * hidden,
+              lambda: tsl.tp_fused_qkv_split(wqkv, None, H, hd, P, r, w_out=b["wq"][r]), cs)
+        T.run("slice", f"wo P{P}", 0, 2 * 2 * hidden * hidden // P,
+              lambda: tsl.tp_plan_shard_slice(wo, None, "rowwise", P, r, w_out=b["wo"][r]), cs)
+        T.run("slice", f"w1 P{P}", 0, 2 * 2 * ffn // P * hidden,
+              lambda: tsl.tp_plan_shard_slice(w1, None, "colwise", P, r, w_out=b["w1"][r]), cs)
+        T.run("slice", f"w2 P{P}", 0, 2 * 2 * hidden * ffn // P,
+              lambda: tsl.tp_plan_shard_slice(w2, None, "rowwise", P, r, w_out=b["w2"][r]), cs)
+        mark(cs, ("w ready", P, r))
+
+    def gemm_rank(P, r):
+        """Rank r's four projections."""
+        b = bufs[P]
+        kq = 3 * H // P * hd
+        k_loc = hidden // P
+        wait(ms, ("w ready", P, r))
+        f, by = gemm_cost(M, kq, hidden, 2)
+        T.run("gemm", f"colwise {M}x{kq}x{hidden}", f, by,
+              lambda: tsl.tp_linear_colwise(x, b["wq"][r], out=b["q"][r]), ms)
+        f, by = gemm_cost(M, hidden, k_loc, 4)
+        T.run("gemm", f"rowwise {M}x{hidden}x{k_loc}", f, by,
+              lambda: tsl.tp_linear_rowwise(A[:, r * k_loc:(r + 1) * k_loc], b["wo"][r],
+                                            out=b["po"][r]), ms)
+        f, by = gemm_cost(M, ffn // P, hidden, 2)
+        T.run("gemm", f"colwise+gelu {M}x{ffn // P}x{hidden}", f, by,
+              lambda: tsl.tp_linear_colwise(x, b["w1"][r], act="gelu_tanh", out=b["h"][r]), ms)
+        f, by = gemm_cost(M, hidden, ffn // P, 4)
+        T.run("gemm", f"rowwise {M}x{hidden}x{ffn // P}", f, by,
+              lambda: tsl.tp_linear_rowwise(b["h"][r], b["w2"][r], out=b["pd"][r]), ms)
+        mark(ms, ("w read", P, r))
+
     def step():
         for P in tps:
             b = bufs[P]
-            kq = 3 * H // P * hd
-            # shard every weight for every rank (index kernels)
             for r in range(P):
-                wait(cs, ("w read", P, r))
-                T.run("slice", f"qkv P{P}", 0, 2 * 2 * kq * hidden,
-                      lambda: tsl.tp_fused_qkv_split(wqkv, None, H, hd, P, r, w_out=b["wq"][r]), cs)
-                T.run("slice", f"wo P{P}", 0, 2 * 2 * hidden * hidden // P,
-                      lambda: tsl.tp_plan_shard_slice(wo, None, "rowwise", P, r, w_out=b["wo"][r]), cs)
-                T.run("slice", f"w1 P{P}", 0, 2 * 2 * ffn // P * hidden,
-                      lambda: tsl.tp_plan_shard_slice(w1, None, "colwise", P, r, w_out=b["w1"][r]), cs)
-                T.run("slice", f"w2 P{P}", 0, 2 * 2 * hidden * ffn // P,
-                      lambda: tsl.tp_plan_shard_slice(w2, None, "rowwise", P, r, w_out=b["w2"][r]), cs)
-                mark(cs, ("w ready", P, r))
-            # every rank's projections
-            k_loc = hidden // P
+                slice_rank(P, r)
             wait(ms, ("out read", P))
             for r in range(P):
-                wait(ms, ("w ready", P, r))
-                f, by = gemm_cost(M, kq, hidden, 2)
-                T.run("gemm", f"colwise {M}x{kq}x{hidden}", f, by,
-                      lambda: tsl.tp_linear_colwise(x, b["wq"][r], out=b["q"][r]), ms)
-                f, by = gemm_cost(M, hidden, k_loc, 4)
-                T.run("gemm", f"rowwise {M}x{hidden}x{k_loc}", f, by,
-                      lambda: tsl.tp_linear_rowwise(A[:, r * k_loc:(r + 1) * k_loc], b["wo"][r],
-                                                    out=b["po"][r]), ms)
-                f, by = gemm_cost(M, ffn // P, hidden, 2)
-                T.run("gemm", f"colwise+gelu {M}x{ffn // P}x{hidden}", f, by,
-                      lambda: tsl.tp_linear_colwise(x, b["w1"][r], act="gelu_tanh", out=b["h"][r]), ms)
-                f, by = gemm_cost(M, hidden, ffn // P, 4)
-                T.run("gemm", f"rowwise {M}x{hidden}x{ffn // P}", f, by,
-                      lambda: tsl.tp_linear_rowwise(b["h"][r], b["w2"][r], out=b["pd"][r]), ms)
-                mark(ms, ("w read", P, r))
+                gemm_rank(P, r)
             mark(ms, ("out ready", P))
             # layer-boundary combines
             wait(cs, ("out ready", P))
