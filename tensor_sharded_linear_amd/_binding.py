@@ -384,14 +384,11 @@ def tp_load_shard(path: str, name: str, style: str = "colwise", tp_degree: int =
     GPU tensor of the file's dtype: ``[rows, cols]``, or ``[cols]`` for a bias."""
     lib = load_library()
     rows, cols, dt = tp_load_shard_shape(path, name, style, tp_degree, rank, blocks=blocks)
-    one_d = False
     if out is None:
         dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
         if dev.type != "cuda":
             raise TypeError("tp_load_shard writes GPU memory (there is no CPU path)")
-        # a 1-D tensor comes back 1-D
-        n_dims = _header_ndim(path, name)
-        one_d = n_dims == 1
+        one_d = _header_ndim(path, name) == 1   # a 1-D tensor comes back 1-D
         out = torch.empty((cols,) if one_d else (rows, cols), dtype=dt, device=dev)
     if not isinstance(out, torch.Tensor) or not out.is_cuda or not out.is_contiguous() or out.dtype != dt:
         raise ValueError(f"out must be a contiguous {dt} GPU tensor")
@@ -406,12 +403,12 @@ def tp_load_shard(path: str, name: str, style: str = "colwise", tp_degree: int =
 
 
 def _header_ndim(path: str, name: str) -> int:
-    """Rank of tensor ``name``: a 1-D query reports rows == 1 and so does a [1, n] weight;
-    the library's colwise query of tp_degree 1 tells them apart by the row count."""
+    """Number of dimensions (1 or 2) of tensor ``name``, from two shape queries: a 1-D tensor
+    and a [1, n] weight both report one row, but only the weight accepts a rowwise cut."""
     rows, _, _ = tp_load_shard_shape(path, name, "colwise", 1, 0)
     if rows != 1:
         return 2
-    try:  # a rowwise cut of a 1-D tensor is rejected, of a [1, n] weight accepted
+    try:
         tp_load_shard_shape(path, name, "rowwise", 1, 0)
         return 2
     except TPValueError:
