@@ -16,7 +16,7 @@ namespace {
 
 thread_local char g_msg[tpl::kLastErrorBytes] = "";
 
-tp_status fail(tp_status s, const char *fmt, ...)
+__attribute__((format(printf, 2, 3))) tp_status fail(tp_status s, const char *fmt, ...)
 {
     va_list ap;
     va_start(ap, fmt);

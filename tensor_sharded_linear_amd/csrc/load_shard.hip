@@ -308,7 +308,7 @@ class JsonReader {
 // --------------------------------------------------------------------------
 // Errors (the message buffer is the one tp_last_error() returns).
 // --------------------------------------------------------------------------
-tp_status fail(tp_status s, const char *fmt, ...)
+__attribute__((format(printf, 2, 3))) tp_status fail(tp_status s, const char *fmt, ...)
 {
     va_list ap;
     va_start(ap, fmt);
