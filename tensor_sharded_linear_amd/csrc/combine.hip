@@ -10,7 +10,10 @@
 // HBM-bound: each thread owns four consecutive columns of R rows and issues
 // all R * P 16-byte loads before summing.  The kernel is templated on a bound
 // PMAX >= P so that its registers match P, and takes R = 2 rows for P <= 4 to
-// keep enough loads in flight.
+// keep enough loads in flight.  The output is stored non-temporally (whole
+// 16-byte vectors of consecutive columns): left dirty in the caches, it was
+// written back during the kernels that followed, and those ran slower (the
+// GEMMs by 1%, the CONCAT by 4%).
 #include "tp_internal.h"
 
 namespace tpl {
@@ -57,9 +60,9 @@ __global__ __launch_bounds__(kThreads) void combine_sum_kernel(SumProblem a)
                 const int64_t o = row * a.ld_out + c;
                 if (OUT_BF16) {
                     const bf16x4 r = bf16x4{(__bf16)s[0], (__bf16)s[1], (__bf16)s[2], (__bf16)s[3]};
-                    *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint16_t *>(a.out) + o) = r;
+                    __builtin_nontemporal_store(r, reinterpret_cast<bf16x4 *>(reinterpret_cast<uint16_t *>(a.out) + o));
                 } else {
-                    *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + o) = s;
+                    __builtin_nontemporal_store(s, reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + o));
                 }
             }
         } else {
