@@ -652,6 +652,24 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / max(args.steps, 1)
     cats, shapes = T.summary()
 
+    # Outside the step: the colwise adaLN GEMV for each number of conditioning rows the
+    # workload allows (1 to 4), every rank's shard in turn, timed like the step's kernels.
+    gemv_rows = {}
+    for nb in [n for n in range(1, B_ADA + 1)] * 2:   # the first pass over the row counts is a warm-up
+        Tb = Timer(torch)
+        Tb.on = True
+        ys = [torch.empty(nb, n_ada, dtype=torch.bfloat16, device=dev) for _ in range(P_ADA)]
+        for _ in range(3):
+            for r in range(P_ADA):
+                Tb.run("gemv", f"B{nb}", 2.0 * nb * n_ada * hidden, 2.0 * n_ada * hidden + 2.0 * nb * (hidden + n_ada),
+                       lambda: tsl.tp_linear_colwise(c_ada[:nb], ada_w[r], out=ys[r]), ms)
+            Tb.flush()
+        torch.cuda.synchronize()
+        c = Tb.summary()[0]["gemv"]
+        gemv_rows[str(nb)] = dict(avg_us=round(c["ms"] * 1e3 / c["launches"], 2),
+                                  gbs=round(c["bytes"] / (c["ms"] * 1e-3) / 1e9, 1),
+                                  pct_hbm_peak=round(100 * c["bytes"] / (c["ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 1))
+
     def gbs(c):
         return c["bytes"] / (c["ms"] * 1e-3) / 1e9 if c["ms"] > 0 else 0.0
 
@@ -705,6 +723,7 @@ def main():
         "kernels": kernels,
         "pct_mfma_peak_whole_step": round(100 * lin_flops_step / (ms_per_step * 1e-3) / 1e12
                                           / PEAK_BF16_TFLOPS, 1),
+        "adaln_gemv_by_rows": gemv_rows,
     }
     if args.detail:
         for k, s in sorted(shapes.items()):
