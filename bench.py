@@ -70,6 +70,15 @@ def parse():
     ap.add_argument("--load-tp", type=int, default=4)
     ap.add_argument("--load-dir", default=None, help="directory for the synthetic checkpoint (default: a temp dir)")
     ap.add_argument("--load-child", nargs=4, metavar=("METHOD", "TP", "PATH", "OUT_JSON"), help=argparse.SUPPRESS)
+    ap.add_argument("--configs", metavar="OUT_MD",
+                    help="per-call table instead of the step: every call of the tiny MLP (tp 2), the attention "
+                         "projections (hidden 3072, tp 4), the large MLP (tp 4) and the adaLN GEMV (tp 4, 1-4 "
+                         "rows) for rank 0, cold (a 512 MiB read before each call) and warm, median of --steps "
+                         "calls, each against its roofline; the oracle timed beside each workload; writes a "
+                         "markdown table to OUT_MD and one JSON line to stdout")
+    ap.add_argument("--configs-trace", metavar="TRACE_CSV",
+                    help="no GPU: from the rocprofv3 kernel trace of a --configs run, print per-kernel medians "
+                         "of the dispatches right after the cache-flush read (cold) and of the others (warm)")
     return ap.parse_args()
 
 
@@ -417,6 +426,12 @@ def main():
     if args.load:
         load_bench(args)
         return
+    if args.configs_trace:
+        configs_trace(args.configs_trace)
+        return
+    if args.configs:
+        configs_bench(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU's share on one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) "
@@ -733,6 +748,261 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+# ---------------------------------------------------------------------------------------------
+# per-call table of the named workloads (rank 0 of each), cold and warm
+# ---------------------------------------------------------------------------------------------
+
+FLUSH_BYTES = 512 << 20  # twice the 256 MB Infinity Cache: reading it evicts every operand
+
+
+def configs_bench(args):
+    """Time every call of the tiny MLP, attention, large-MLP and adaLN workloads (rank 0).
+
+    Cold: a 512 MiB read runs before each call, so operands come from HBM; the figure is the
+    median of --steps calls, each timed by its own HIP event pair.  Warm: --steps calls back to
+    back under one event pair, averaged.  MFMA calls report TFLOP/s and the roofline fraction
+    max(flops / 2.5 PF, bytes / 8 TB/s) / time; HBM calls report GB/s of algorithmic bytes."""
+    import numpy as np
+    import torch
+
+    import synth_inputs as si
+    import tensor_sharded_linear_amd as tsl
+
+    if not torch.cuda.is_available():
+        print("bench.py --configs needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tsl.load_library()
+    reps, warm = max(args.steps, 20), max(args.warmup, 5)
+    # A read-only flush: a fill would leave dirty lines that the timed call then writes back.
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def cold_us(fn):
+        """Median over reps of one call after the cache flush; the flush keeps the GPU busy while
+        the host enqueues the events and the call, so no launch gap is timed (the event pair
+        itself adds 2-3 us)."""
+        for _ in range(warm):
+            fn()
+        evs = []
+        for _ in range(reps):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+
+    def warm_us(fn):
+        """Average of reps back-to-back calls under one event pair; a spin kernel first keeps the
+        GPU busy while the host enqueues them all."""
+        for _ in range(warm):
+            fn()
+        torch.cuda._sleep(40000 * reps)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    rows = []
+
+    def call(cfg, name, fn, flops, nbytes):
+        c, w = cold_us(fn), warm_us(fn)
+        if flops:
+            t_roof = max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
+            bound = "mfma" if flops / (PEAK_BF16_TFLOPS * 1e12) >= nbytes / (PEAK_HBM_GBS * 1e9) else "hbm"
+            r = dict(config=cfg, call=name, bound=bound, flops=flops, bytes=nbytes, cold_us=round(c, 2),
+                     warm_us=round(w, 2), tflops=round(flops / c / 1e6, 1),
+                     pct_mfma_peak=round(100 * flops / c / 1e6 / PEAK_BF16_TFLOPS, 1),
+                     roofline_frac=round(t_roof / c, 3))
+        else:
+            r = dict(config=cfg, call=name, bound="hbm", flops=0, bytes=nbytes, cold_us=round(c, 2),
+                     warm_us=round(w, 2), gbs=round(nbytes / c / 1e3, 1),
+                     pct_hbm_peak=round(100 * nbytes / c / 1e3 / PEAK_HBM_GBS, 1), roofline_frac=None)
+            r["roofline_frac"] = round(r["pct_hbm_peak"] / 100, 3)
+        rows.append(r)
+        print(f"# {cfg:10s} {name:44s} cold {c:8.1f} us  warm {w:8.1f} us", file=sys.stderr, flush=True)
+
+    def gemm_bytes(m_, n_, k_, out_es, bias=False):
+        return 2 * (m_ * k_ + n_ * k_) + out_es * m_ * n_ + (2 * n_ if bias else 0)
+
+    oracle_rows = []
+    # tiny MLP, tp 2: both ranks' slices and GEMMs, then the SUM with the bias
+    wl = si.workload("tiny_mlp")
+    a = {k: up(v) for k, v in wl.arrays.items()}
+    P, M, D, F = 2, wl.meta["M"], wl.meta["hidden"], wl.meta["ffn"]
+    f = F // P
+    w1s = [tsl.tp_plan_shard_slice(a["w1"], a["b1"], "colwise", P, r) for r in range(P)]
+    w2s = [tsl.tp_plan_shard_slice(a["w2"], None, "rowwise", P, r)[0] for r in range(P)]
+    hs = [tsl.tp_linear_colwise(a["x"], w, b, act="gelu_tanh") for w, b in w1s]
+    parts = [tsl.tp_linear_rowwise(h, w) for h, w in zip(hs, w2s)]
+    call("tiny_mlp", f"slice W1 colwise + b1 [{f},{D}]", lambda: tsl.tp_plan_shard_slice(
+        a["w1"], a["b1"], "colwise", P, 0, w_out=w1s[0][0], b_out=w1s[0][1]), 0, 2 * 2 * (f * D + f))
+    call("tiny_mlp", f"slice W2 rowwise [{D},{f}]", lambda: tsl.tp_plan_shard_slice(
+        a["w2"], None, "rowwise", P, 0, w_out=w2s[0]), 0, 2 * 2 * D * f)
+    call("tiny_mlp", f"colwise+b1+GELU {M}x{f}x{D}", lambda: tsl.tp_linear_colwise(
+        a["x"], w1s[0][0], w1s[0][1], act="gelu_tanh", out=hs[0]), 2 * M * f * D, gemm_bytes(M, f, D, 2, True))
+    call("tiny_mlp", f"rowwise {M}x{D}x{f} -> f32", lambda: tsl.tp_linear_rowwise(hs[0], w2s[0], out=parts[0]),
+         2 * M * D * f, gemm_bytes(M, D, f, 4))
+    y = torch.empty(M, D, dtype=torch.float32, device=dev)
+    call("tiny_mlp", f"SUM of {P} x [{M},{D}] f32 + b2", lambda: tsl.tp_partial_combine(
+        parts, "sum", bias=a["b2"], out=y), 0, P * 4 * M * D + 4 * M * D + 2 * D)
+    oracle_rows.append(_oracle_config("tiny_mlp", wl))
+    del a, w1s, w2s, hs, parts
+
+    # attention projections, tp 4, rank 0: QKV split, colwise QKV, rowwise out-proj on A's column slice
+    wl = si.workload("attention_proj")
+    a = {k: up(v) for k, v in wl.arrays.items()}
+    P, M, D, H, hd = 4, wl.meta["M"], wl.meta["hidden"], wl.meta["heads"], wl.meta["head_dim"]
+    kq, kl = 3 * H // P * hd, D // P
+    wq, _ = tsl.tp_fused_qkv_split(a["w_qkv"], None, H, hd, P, 0)
+    wo, _ = tsl.tp_plan_shard_slice(a["w_o"], None, "rowwise", P, 0)
+    q = torch.empty(M, kq, dtype=torch.bfloat16, device=dev)
+    po = torch.empty(M, D, dtype=torch.float32, device=dev)
+    call("attention", f"QKV split (head-aligned) [{kq},{D}]", lambda: tsl.tp_fused_qkv_split(
+        a["w_qkv"], None, H, hd, P, 0, w_out=wq), 0, 2 * 2 * kq * D)
+    call("attention", f"slice W_o rowwise [{D},{kl}]", lambda: tsl.tp_plan_shard_slice(
+        a["w_o"], None, "rowwise", P, 0, w_out=wo), 0, 2 * 2 * D * kl)
+    call("attention", f"colwise QKV {M}x{kq}x{D}", lambda: tsl.tp_linear_colwise(a["x"], wq, out=q),
+         2 * M * kq * D, gemm_bytes(M, kq, D, 2))
+    call("attention", f"rowwise out-proj {M}x{D}x{kl} -> f32", lambda: tsl.tp_linear_rowwise(
+        a["a"][:, :kl], wo, out=po), 2 * M * D * kl, gemm_bytes(M, D, kl, 4))
+    oracle_rows.append(_oracle_config("attention", wl))
+    del a, wq, wo, q, po
+
+    # large MLP, tp 4, rank 0
+    wl = si.workload("mlp_large")
+    a = {k: up(v) for k, v in wl.arrays.items()}
+    P, M, D, F = 4, wl.meta["M"], wl.meta["hidden"], wl.meta["ffn"]
+    f = F // P
+    w1, _ = tsl.tp_plan_shard_slice(a["w1"], None, "colwise", P, 0)
+    w2, _ = tsl.tp_plan_shard_slice(a["w2"], None, "rowwise", P, 0)
+    h = tsl.tp_linear_colwise(a["x"], w1, act="gelu_tanh")
+    pd = torch.empty(M, D, dtype=torch.float32, device=dev)
+    call("mlp", f"slice W1 colwise [{f},{D}]", lambda: tsl.tp_plan_shard_slice(
+        a["w1"], None, "colwise", P, 0, w_out=w1), 0, 2 * 2 * f * D)
+    call("mlp", f"slice W2 rowwise [{D},{f}]", lambda: tsl.tp_plan_shard_slice(
+        a["w2"], None, "rowwise", P, 0, w_out=w2), 0, 2 * 2 * D * f)
+    call("mlp", f"colwise+GELU {M}x{f}x{D}", lambda: tsl.tp_linear_colwise(
+        a["x"], w1, act="gelu_tanh", out=h), 2 * M * f * D, gemm_bytes(M, f, D, 2))
+    call("mlp", f"rowwise {M}x{D}x{f} -> f32", lambda: tsl.tp_linear_rowwise(h, w2, out=pd),
+         2 * M * D * f, gemm_bytes(M, D, f, 4))
+    oracle_rows.append(_oracle_config("mlp", wl))
+    del a, w1, w2, h, pd
+
+    # adaLN, tp 4, rank 0: the colwise slice, then the GEMV for 1..4 conditioning rows
+    wl = si.workload("adaln")
+    a = {k: up(v) for k, v in wl.arrays.items()}
+    P, D = 4, wl.meta["hidden"]
+    n = wl.meta["out"] // P
+    wa, _ = tsl.tp_plan_shard_slice(a["w_ada"], None, "colwise", P, 0)
+    call("adaln", f"slice W_ada colwise [{n},{D}]", lambda: tsl.tp_plan_shard_slice(
+        a["w_ada"], None, "colwise", P, 0, w_out=wa), 0, 2 * 2 * n * D)
+    for B in range(1, 5):
+        yb = torch.empty(B, n, dtype=torch.bfloat16, device=dev)
+        c = a["c"][:B]
+        call("adaln", f"colwise GEMV {B} row{'s' if B > 1 else ''} x [{n},{D}]", lambda c=c, yb=yb:
+             tsl.tp_linear_colwise(c, wa, out=yb), 2 * B * n * D, 2 * n * D)
+    oracle_rows.append(_oracle_config("adaln", wl))
+    del a, wa
+
+    out = {"configs": rows, "cpu_baseline": oracle_rows, "reps": reps, "warmup": warm,
+           "cold": f"{FLUSH_BYTES >> 20} MiB read before each call"}
+    md = ["| workload | call | bound | cold µs | warm µs | cold rate | % of peak | roofline frac |",
+          "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        rate = f"{r['tflops']} TFLOP/s" if r["flops"] else f"{r['gbs']} GB/s"
+        pct = r.get("pct_mfma_peak", r.get("pct_hbm_peak"))
+        md.append(f"| {r['config']} | {r['call']} | {r['bound']} | {r['cold_us']} | {r['warm_us']} | {rate} | "
+                  f"{pct} | {r['roofline_frac']} |")
+    md += ["", "| workload | oracle sample | oracle seconds | oracle GFLOP/s | threads |", "|---|---|---|---|---|"]
+    for o in oracle_rows:
+        md.append(f"| {o['config']} | {o['sample']} | {o['seconds']} | {o['gflops']} | {o['cores']} |")
+    with open(args.configs, "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    print(json.dumps(out), flush=True)
+
+
+def configs_trace(path):
+    """Cold and warm medians per kernel (name and grid) from a --configs run's kernel trace.
+
+    A dispatch is cold when the dispatch before it is the flush read (torch's reduction
+    kernel).  Unlike the call table's event pairs, these durations carry no event overhead."""
+    import csv
+    import statistics
+
+    recs = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    groups, prev = {}, ""
+    for r in recs:
+        name = r["Kernel_Name"]
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        short = name.replace("void ", "").replace("tpl::(anonymous namespace)::", "").split("(")[0]
+        if short.startswith(("gemm_", "gemv_", "copy_", "combine_")):
+            g = groups.setdefault((short, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"])), ([], []))
+            g[0 if "reduce" in prev else 1].append(us)
+        prev = name
+    print("| kernel | grid (threads) | workgroup | cold dispatches | cold median µs | warm dispatches | warm median µs |")
+    print("|---|---|---|---|---|---|---|")
+    for (k, grid, wg), (c, w) in groups.items():
+        med = lambda v: f"{statistics.median(v):.1f}" if v else "-"
+        print(f"| `{k}` | {grid} | {wg} | {len(c)} | {med(c)} | {len(w)} | {med(w)} |")
+
+
+def _oracle_config(cfg, wl):
+    """The oracle (as it stands) on the same workload's rank-0 GEMM work: whole for the tiny MLP
+    and the adaLN GEMV, a 192-row sample of the 4608 tokens for the attention and MLP workloads."""
+    import numpy as np
+
+    import oracle
+
+    a, meta = wl.arrays, wl.meta
+    threads = oracle.default_threads()
+    t = time.perf_counter()
+    if cfg == "tiny_mlp":
+        P, D, F = 2, meta["hidden"], meta["ffn"]
+        parts = []
+        for r in range(P):
+            w1, b1 = oracle.shard_colwise(a["w1"], a["b1"], P, r)
+            h = oracle.bf16_round(oracle.colwise(a["x"], w1, b1, act=oracle.ACT_GELU_TANH, threads=threads))
+            parts.append(oracle.linear(h, oracle.shard_rowwise(a["w2"], P, r), threads=threads))
+        oracle.combine_sum(parts, a["b2"])
+        flops, sample = 2.0 * meta["M"] * 2 * F * D, "whole workload (both ranks, SUM)"
+    elif cfg == "attention":
+        P, D, H, hd = 4, meta["hidden"], meta["heads"], meta["head_dim"]
+        rows = np.arange(0, meta["M"], meta["M"] // 192)
+        wq, _ = oracle.qkv_split(a["w_qkv"], None, H, hd, P, 0)
+        oracle.colwise(a["x"], wq, rows=rows, threads=threads)
+        oracle.rowwise(a["a"], 0, P, oracle.shard_rowwise(a["w_o"], P, 0), rows=rows, threads=threads)
+        flops = 2.0 * len(rows) * (wq.shape[0] * D + D * D // P)
+        sample = f"{len(rows)} of {meta['M']} token rows, rank 0 (QKV colwise, out-proj rowwise)"
+    elif cfg == "mlp":
+        P, D, F = 4, meta["hidden"], meta["ffn"]
+        rows = np.arange(0, meta["M"], meta["M"] // 192)
+        w1, _ = oracle.shard_colwise(a["w1"], None, P, 0)
+        h = oracle.bf16_round(oracle.colwise(a["x"], w1, act=oracle.ACT_GELU_TANH, rows=rows, threads=threads))
+        oracle.linear(h, oracle.shard_rowwise(a["w2"], P, 0), threads=threads)
+        flops = 2.0 * len(rows) * 2 * (F // P) * D
+        sample = f"{len(rows)} of {meta['M']} token rows, rank 0 (FFN-up colwise+GELU, FFN-down rowwise)"
+    else:
+        P, D = 4, meta["hidden"]
+        w, _ = oracle.shard_colwise(a["w_ada"], None, P, 0)
+        for B in range(1, 5):
+            oracle.colwise(a["c"][:B], w, threads=threads)
+        flops = 2.0 * (1 + 2 + 3 + 4) * w.shape[0] * D
+        sample = "whole workload (rank 0, 1 to 4 rows)"
+    dt = time.perf_counter() - t
+    return {"config": cfg, "kind": "oracle", "sample": sample, "seconds": round(dt, 3),
+            "gflops": round(flops / dt / 1e9, 2), "cores": threads}
 
 
 def cpu_baseline(target_s: float):
