@@ -100,8 +100,9 @@ typedef enum { TP_COMBINE_SUM = 0, TP_COMBINE_CONCAT = 1 } tp_combine;
  * fp32, one rounding to y_dtype (round to nearest even for bf16).
  * Small M (up to 8 rows, K <= 8192) uses a weight-streaming kernel (the skinny adaLN modulation shape),
  * larger M, and SwiGLU at any M, the tiled MFMA kernel; both obey the same contract.
- * Requires K % 64 == 0 and n_shard % 16 == 0, and each operand view (rows x
- * leading dimension) below 2 GiB (TP_ERR_UNSUPPORTED otherwise).
+ * Requires K % 64 == 0 and n_shard % 16 == 0, each operand view (rows x
+ * leading dimension) below 2 GiB, row strides of at most 2^31 elements and
+ * at most 2^22 output tiles of 192 x 256 (TP_ERR_UNSUPPORTED otherwise).
  */
 tp_status tp_linear_colwise(const void *x, int64_t ldx, const void *w_shard, int64_t ldw,
                             const void *bias, void *y, int64_t ldy, tp_dtype y_dtype,
@@ -122,8 +123,9 @@ tp_status tp_linear_colwise(const void *x, int64_t ldx, const void *w_shard, int
  *   partial [M, N]        fp32, row stride ldp (>= N, multiple of 4)
  *
  * Arithmetic: bf16 products, fp32 accumulation, fp32 store.
- * Requires k_shard % 64 == 0 and N % 16 == 0, and each operand view (rows x
- * leading dimension) below 2 GiB (TP_ERR_UNSUPPORTED otherwise).
+ * Requires k_shard % 64 == 0 and N % 16 == 0, each operand view (rows x
+ * leading dimension) below 2 GiB, row strides of at most 2^31 elements and
+ * at most 2^22 output tiles of 192 x 256 (TP_ERR_UNSUPPORTED otherwise).
  */
 tp_status tp_linear_rowwise(const void *x_shard, int64_t ldx, const void *w_shard, int64_t ldw,
                             float *partial, int64_t ldp, int64_t M, int64_t N, int64_t k_shard,
@@ -168,7 +170,8 @@ tp_status tp_linear_rowwise_split_input(const void *x_full, int64_t ldx, int64_t
  * dtype: TP_BF16 or TP_F32 element size; the copy is bit-exact.
  *
  * Errors: TP_ERR_NOT_DIVISIBLE if P does not divide H; TP_ERR_INVALID_ARG for
- * P < 1, rank outside [0, P), non-positive sizes, or null/misaligned pointers.
+ * P < 1, rank outside [0, P), non-positive sizes, or null/misaligned pointers;
+ * TP_ERR_UNSUPPORTED for a fused weight of more than 2^30 rows (3*H*hd).
  * Only 4-byte alignment is required here.
  */
 tp_status tp_fused_qkv_split(const void *w_qkv, const void *b_qkv, void *w_shard, void *b_shard,
@@ -202,7 +205,8 @@ tp_status tp_fused_qkv_split(const void *w_qkv, const void *b_qkv, void *w_shard
  *
  * Errors: TP_ERR_NOT_DIVISIBLE when the blocks do not tile n_out per the
  * constraints of [TP] "Constraints and verification"; TP_ERR_INVALID_ARG for
- * bad counts, dtypes, pointers or leading dimensions.
+ * bad counts, dtypes, pointers or leading dimensions; TP_ERR_UNSUPPORTED for
+ * leading dimensions above 2^31 elements.
  */
 tp_status tp_partial_combine(const void *const *parts, int num_parts, int64_t ld_part, void *out,
                              int64_t ld_out, tp_dtype in_dtype, tp_dtype out_dtype,

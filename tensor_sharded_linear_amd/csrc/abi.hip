@@ -38,6 +38,11 @@ int elem_size(tp_dtype d) { return d == TP_BF16 ? 2 : (d == TP_F32 ? 4 : 0); }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int64_t kMaxOperandBytes = (int64_t)1 << 31;
+// Row strides above 2^31 elements are rejected, so that no offset product overflows.
+constexpr int64_t kMaxLd = (int64_t)1 << 31;
+// Output tiles of one tiled-GEMM launch (each a 512-thread workgroup): the
+// launch's thread count must stay below 2^32.
+constexpr int64_t kMaxTiles = (int64_t)1 << 22;
 constexpr int kMaxBlocks = 16;
 
 // Common checks of the two compute entry points.  Returns TP_OK when the
@@ -52,6 +57,8 @@ tp_status check_linear(const char *fn, const void *x, int64_t ldx, const void *w
                     (long long)M, (long long)N, (long long)K);
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return fail(TP_ERR_UNSUPPORTED, "%s: dimensions above 2^30 are not supported", fn);
+    if (ldx > kMaxLd || ldw > kMaxLd || ldy > kMaxLd)
+        return fail(TP_ERR_UNSUPPORTED, "%s: row strides above 2^31 elements are not supported", fn);
     if (K % 64 != 0)
         return fail(TP_ERR_UNSUPPORTED, "%s: K=%lld must be a multiple of 64", fn, (long long)K);
     if (N % 16 != 0)
@@ -68,6 +75,9 @@ tp_status check_linear(const char *fn, const void *x, int64_t ldx, const void *w
     // The kernels address each operand by 32-bit byte offsets from its base.
     if (((N - 1) * ldw + K) * 2 >= kMaxOperandBytes || (M > 0 && ((M - 1) * ldx + K) * 2 >= kMaxOperandBytes))
         return fail(TP_ERR_UNSUPPORTED, "%s: an operand spans 2 GiB or more", fn);
+    if ((M + 191) / 192 * ((N + 255) / 256) > kMaxTiles)
+        return fail(TP_ERR_UNSUPPORTED, "%s: an output of %lld x %lld needs more than 2^22 tiles", fn,
+                    (long long)M, (long long)N);
     if (!w || !aligned(w, 16))
         return fail(TP_ERR_INVALID_ARG, "%s: weight pointer is null or not 16-byte aligned", fn);
     if (bias && !aligned(bias, 8))
@@ -245,6 +255,8 @@ tp_status tp_fused_qkv_split(const void *w_qkv, const void *b_qkv, void *w_shard
         return fail(TP_ERR_INVALID_ARG, "%s: rank=%d outside [0, %d)", fn, rank, tp_degree);
     if (num_heads < 1 || head_dim < 1 || K < 1 || num_heads > kMaxDim || head_dim > kMaxDim || K > kMaxDim)
         return fail(TP_ERR_INVALID_ARG, "%s: num_heads, head_dim and K must be in [1, 2^30]", fn);
+    if (3 * num_heads * head_dim > kMaxDim)
+        return fail(TP_ERR_UNSUPPORTED, "%s: a fused weight of more than 2^30 rows is not supported", fn);
     if (num_heads % tp_degree != 0)
         return fail(TP_ERR_NOT_DIVISIBLE, "%s: tp_degree=%d does not divide num_heads=%lld", fn, tp_degree,
                     (long long)num_heads);
@@ -284,6 +296,8 @@ tp_status tp_partial_combine(const void *const *parts, int num_parts, int64_t ld
         return fail(TP_ERR_INVALID_ARG, "%s: parts (host array) is null", fn);
     if (M < 0 || n_part < 1 || M > kMaxDim || n_part > kMaxDim)
         return fail(TP_ERR_INVALID_ARG, "%s: need 0 <= M <= 2^30 and 1 <= n_part <= 2^30", fn);
+    if (ld_part > kMaxLd || ld_out > kMaxLd)
+        return fail(TP_ERR_UNSUPPORTED, "%s: row strides above 2^31 elements are not supported", fn);
     if (mode == TP_COMBINE_SUM) {
         if (in_dtype != TP_F32)
             return fail(TP_ERR_INVALID_ARG, "%s: SUM combines fp32 partials (in_dtype must be TP_F32)", fn);

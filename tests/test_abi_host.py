@@ -86,6 +86,12 @@ def rowwise(**kw):
     # operand views of 2 GiB or more: the kernels use 32-bit byte offsets
     (dict(M=1 << 20, ldx=1 << 10, ldw=1 << 10, K=1 << 10), B.TP_ERR_UNSUPPORTED),
     (dict(N=1 << 20, ldy=1 << 20, ldx=1 << 10, ldw=1 << 10, K=1 << 10), B.TP_ERR_UNSUPPORTED),
+    # strides whose products with a row count would overflow 64 bits
+    (dict(ldw=1 << 62), B.TP_ERR_UNSUPPORTED),
+    (dict(ldx=1 << 62), B.TP_ERR_UNSUPPORTED),
+    (dict(ldy=(1 << 61) + 512), B.TP_ERR_UNSUPPORTED),
+    # more output tiles than one launch can hold (2^22): 2^21 x 2^21 with one-row operands
+    (dict(M=1 << 21, N=1 << 21, ldy=1 << 21, ldx=64, ldw=64, K=64), B.TP_ERR_UNSUPPORTED),
 ])
 def test_colwise_validation(kw, status):
     assert colwise(**kw) == status
@@ -157,6 +163,7 @@ def qkv(**kw):
     (dict(b=A3), B.TP_ERR_INVALID_ARG),       # bias in without bias out
     (dict(w=None), B.TP_ERR_INVALID_ARG),
     (dict(dtype=9), B.TP_ERR_INVALID_ARG),
+    (dict(H=1 << 20, hd=1 << 10, P=1), B.TP_ERR_UNSUPPORTED),  # 3 * 2^30 fused rows
 ])
 def test_qkv_split_validation(kw, status):
     assert qkv(**kw) == status
@@ -256,6 +263,8 @@ def test_combine_validation():
     assert combine(two, out=A, out_dtype=B.TP_BF16) == B.TP_ERR_INVALID_ARG  # bf16 in place
     assert combine(two, mode=9) == B.TP_ERR_INVALID_ARG
     assert combine(two, M=0) == B.TP_OK
+    assert combine(two, ld_part=1 << 62) == B.TP_ERR_UNSUPPORTED
+    assert combine(two, ld_out=1 << 62) == B.TP_ERR_UNSUPPORTED
     # concat
     cc = dict(mode=B.TP_COMBINE_CONCAT, in_dtype=B.TP_BF16, out_dtype=B.TP_BF16, ld_out=512)
     assert combine(two, **cc, M=0) == B.TP_OK
