@@ -169,6 +169,13 @@ __device__ __forceinline__ Ctx make_ctx()
     return c;
 }
 
+// Waits until this wave's direct-to-LDS loads have written the LDS.  A
+// barrier after it then publishes every wave's loads to the workgroup.  The
+// compiler's own waits do not cover this in every loop shape: a k-step-32
+// variant of this kernel compiled with no load wait before its barrier and read
+// stale tiles.
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // One 16-byte direct-to-LDS load per lane (global_load_lds_dwordx4): lane l
 // writes dst + 16 l bytes.  Kept out of templates: the host pass of a
 // template rejects the LDS address-space argument.
@@ -252,6 +259,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
     Frags<TM> f0, f1;
     __syncthreads();  // the LDS is free: the previous tile's reads are done
     issue(0, 0);
+    wait_dma();
     __syncthreads();
     read_frags(0, 0, f0);
     if (T > 1)
@@ -259,6 +267,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
     for (int t = 0; t < T - 1; ++t) {
         const int st = t & 1;
         TPL_STEP(read_frags(st, 1, f1), mma(f0));
+        wait_dma();
         __syncthreads();
         if (t + 2 < T)
             issue(st, (t + 2) * BK);
