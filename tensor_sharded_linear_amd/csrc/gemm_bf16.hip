@@ -61,9 +61,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define TPL_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
-// The tile height is a template parameter TM, the number of 32-row MFMA
-// blocks per wave: TM = 4 gives 256 x 256 tiles, TM = 3 gives 192 x 256
-// tiles (chosen when they fill the CUs better, see pick_tm).
+// The tile height is a template parameter NXB, the number of 16-row MFMA
+// blocks per wave: NXB = 8, 7, 6 give 256, 224 and 192 x 256 tiles (the one
+// that fills the CUs best for the shape is chosen, see pick_nxb).
 constexpr int BN = 256;
 constexpr int BK = 64;
 constexpr int kThreads = 512;     // 8 waves in a 2 (M) x 4 (N) grid
@@ -73,15 +73,20 @@ constexpr int WN = 64;            // columns of the output owned by one wave
 constexpr int WB = WN / 16;       // 16-row W blocks (16-column MFMA tiles) per wave
 constexpr int kDmaW = (BN * BK * 2) / (kThreads * 16);  // 16-byte DMAs per thread per W tile
 
-template <int TM>
+template <int NXB>
 struct Tile {
-    static constexpr int XB = 2 * TM;    // 16-row X blocks (16-row MFMA tiles) per wave
-    static constexpr int WM = 32 * TM;   // rows of the output owned by one wave
+    static constexpr int XB = NXB;       // 16-row X blocks (16-row MFMA tiles) per wave
+    static constexpr int WM = 16 * NXB;  // rows of the output owned by one wave
     static constexpr int BM = 2 * WM;    // rows of the output tile
-    static constexpr int kDmaX = (BM * BK * 2) / (kThreads * 16);  // 16-byte DMAs per thread per X tile
     static constexpr int kXElems = BM * BK;
+    // 16-byte DMAs per thread per X tile.  One DMA instruction of the
+    // workgroup moves 64 rows; with an odd NXB the last one covers 32 rows and
+    // only waves 0-3 issue it.
+    static constexpr int kDmaX = (BM + 63) / 64;
+    static constexpr bool kDmaXPartial = BM % 64 != 0;
     static constexpr int kStageElems = (BM + BN) * BK;  // X tile + W tile
-    static constexpr int kLdsElems = 2 * kStageElems;   // double buffered: 128 or 112 KiB
+    static constexpr int kLdsElems = 2 * kStageElems;   // double buffered: 128, 120 or 112 KiB
+    static_assert(BM % 32 == 0, "X tile rows: a multiple of 32");
 };
 
 struct GemmParams {
@@ -129,10 +134,10 @@ __device__ __forceinline__ float gelu_tanh(float v)
 }
 
 // One k32 step's operand fragments: per lane 8 bf16 of one row of each of
-// the wave's 2 TM 16-row X blocks and four 16-row W blocks.
-template <int TM>
+// the wave's NXB 16-row X blocks and four 16-row W blocks.
+template <int NXB>
 struct Frags {
-    bf16x8 x[Tile<TM>::XB];
+    bf16x8 x[Tile<NXB>::XB];
     bf16x8 w[WB];
 };
 
@@ -144,7 +149,7 @@ struct Ctx {
     int swz, kh;                  // fragment swizzle and k-quarter
 };
 
-template <int TM>
+template <int NXB>
 __device__ __forceinline__ Ctx make_ctx()
 {
     Ctx c;
@@ -162,7 +167,7 @@ __device__ __forceinline__ Ctx make_ctx()
     // Fragment addressing: lane l reads row (l % 16) of a 16-row block,
     // 16-byte k-chunk (4 s + l / 16) for k32 step s, stored at position
     // chunk ^ ((row >> 1) & 7) = chunk ^ (((l % 16) >> 1) & 7).
-    c.xrow_off = (c.wave_m * Tile<TM>::WM + (c.lane & 15)) * BK;
+    c.xrow_off = (c.wave_m * Tile<NXB>::WM + (c.lane & 15)) * BK;
     c.wrow_off = (c.wave_n * WN + (c.lane & 15)) * BK;
     c.swz = (c.lane >> 1) & 7;
     c.kh = c.lane >> 4;
@@ -192,15 +197,15 @@ __device__ __forceinline__ void dma16(const char *src, uint16_t *dst)
 // projection of the same 32 output columns n0 + 32 q + [0, 32).  Rows past the end are clamped
 // (computed and discarded).  Starts with a barrier, so the LDS may still be in
 // use by the caller's previous tile when it is called.
-template <int TM, bool GATED>
+template <int NXB, bool GATED>
 __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, const Ctx &c, int m0, int n0,
-                                         int kt0, int kt1, f32x4 (&acc)[Tile<TM>::XB][WB])
+                                         int kt0, int kt1, f32x4 (&acc)[Tile<NXB>::XB][WB])
 {
     // Per-lane byte offsets (32-bit: operands are below 2 GiB) from
     // wave-uniform bases, so the DMA uses the scalar-base addressing form.
     const char *xbase = reinterpret_cast<const char *>(p.x) + (int64_t)kt0 * BK * 2;
     const char *wbase = reinterpret_cast<const char *>(p.w) + (int64_t)kt0 * BK * 2;
-    typedef Tile<TM> L;
+    typedef Tile<NXB> L;
     uint32_t xoff[L::kDmaX], woff[kDmaW];
 #pragma unroll
     for (int j = 0; j < L::kDmaX; ++j) {
@@ -221,12 +226,13 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
         const char *wb = wbase + k0 * 2;
 #pragma unroll
         for (int j = 0; j < L::kDmaX; ++j)
-            dma16(xb + xoff[j], xs + (j * kWaves + c.wave) * 512);
+            if (!L::kDmaXPartial || j < L::kDmaX - 1 || (j * kWaves + c.wave) * 512 < L::kXElems)
+                dma16(xb + xoff[j], xs + (j * kWaves + c.wave) * 512);
 #pragma unroll
         for (int j = 0; j < kDmaW; ++j)
             dma16(wb + woff[j], ws + (j * kWaves + c.wave) * 512);
     };
-    auto read_frags = [&](int stage, int s, Frags<TM> &f) {
+    auto read_frags = [&](int stage, int s, Frags<NXB> &f) {
         const uint16_t *xs = lds + stage * L::kStageElems;
         const uint16_t *ws = xs + L::kXElems;
         const int cpos = ((s * 4 + c.kh) ^ c.swz) * 8;
@@ -237,7 +243,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
         for (int j = 0; j < WB; ++j)
             f.w[j] = *reinterpret_cast<const bf16x8 *>(ws + c.wrow_off + j * 16 * BK + cpos);
     };
-    auto mma = [&](const Frags<TM> &f) {
+    auto mma = [&](const Frags<NXB> &f) {
 #pragma unroll
         for (int i = 0; i < L::XB; ++i)
 #pragma unroll
@@ -256,7 +262,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
         __builtin_amdgcn_sched_group_barrier(0x008, L::XB * WB - (L::XB + WB), 0); \
         __builtin_amdgcn_sched_barrier(0); } while (0)
     const int T = kt1 - kt0;
-    Frags<TM> f0, f1;
+    Frags<NXB> f0, f1;
     __syncthreads();  // the LDS is free: the previous tile's reads are done
     issue(0, 0);
     wait_dma();
@@ -295,9 +301,9 @@ constexpr int kActSwiglu = 2;  // W tile = interleaved [gate; up] 32-row blocks,
 // output columns, or 32 with SwiGLU: there its blocks j = 0, 1 hold the gate
 // and j = 2, 3 the up projection of the same 32 columns, and the output is
 // silu(gate + b_gate) * (up + b_up), the bias being [b_gate; b_up] (2 N).
-template <int TM, bool OUT_BF16, bool HAS_BIAS, int ACT>
+template <int NXB, bool OUT_BF16, bool HAS_BIAS, int ACT>
 __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, const Ctx &c, int m0, int n0,
-                                         const f32x4 (&acc)[Tile<TM>::XB][WB])
+                                         const f32x4 (&acc)[Tile<NXB>::XB][WB])
 {
     __syncthreads();  // every wave is done reading the operand stages
     typedef typename std::conditional<OUT_BF16, __bf16, float>::type OutT;
@@ -319,7 +325,7 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, con
     const int rd_row = c.lane / kVecPerRow;
     const int rd_vec = c.lane % kVecPerRow;
 #pragma unroll
-    for (int i = 0; i < Tile<TM>::XB; ++i) {
+    for (int i = 0; i < Tile<NXB>::XB; ++i) {
 #pragma unroll
         for (int j = 0; j < JO; ++j) {
             const int n = n0 + c.wave_n * WNO + j * 16 + ncol;  // N % 16 == 0: n < N covers n + 3
@@ -347,7 +353,7 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, con
             else
                 *reinterpret_cast<f32x4 *>(dst) = v;
         }
-        const int mbase = m0 + c.wave_m * Tile<TM>::WM + i * 16;
+        const int mbase = m0 + c.wave_m * Tile<NXB>::WM + i * 16;
         const int ncol0 = n0 + c.wave_n * WNO + rd_vec * kVec;
 #pragma unroll
         for (int r = 0; r < 16; r += kRowsPerPass) {
@@ -360,11 +366,11 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, con
     }
 }
 
-template <int TM>
-__device__ __forceinline__ void zero(f32x4 (&acc)[Tile<TM>::XB][WB])
+template <int NXB>
+__device__ __forceinline__ void zero(f32x4 (&acc)[Tile<NXB>::XB][WB])
 {
 #pragma unroll
-    for (int i = 0; i < Tile<TM>::XB; ++i)
+    for (int i = 0; i < Tile<NXB>::XB; ++i)
 #pragma unroll
         for (int j = 0; j < WB; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -372,38 +378,41 @@ __device__ __forceinline__ void zero(f32x4 (&acc)[Tile<TM>::XB][WB])
 
 // One BM x 256 output tile per workgroup (BM x 128 output columns with
 // SwiGLU: the tile's 256 weight rows are 128 gate and 128 up rows).
-template <int TM, bool OUT_BF16, bool HAS_BIAS, int ACT>
+template <int NXB, bool OUT_BF16, bool HAS_BIAS, int ACT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_nt_kernel(GemmParams p)
 {
-    constexpr int BM = Tile<TM>::BM;
+    constexpr int BM = Tile<NXB>::BM;
     constexpr bool kGated = ACT == kActSwiglu;
     constexpr int kTileCols = kGated ? BN / 2 : BN;
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[Tile<TM>::kLdsElems];
-    const Ctx c = make_ctx<TM>();
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[Tile<NXB>::kLdsElems];
+    const Ctx c = make_ctx<NXB>();
     int tm, tn;
     tile_of(xcd_contiguous(blockIdx.x, p.tiles_m * p.tiles_n), p, tm, tn);
-    f32x4 acc[Tile<TM>::XB][WB];
-    zero<TM>(acc);
-    mainloop<TM, kGated>(p, lds, c, tm * BM, tn * kTileCols, 0, p.K / BK, acc);
-    epilogue<TM, OUT_BF16, HAS_BIAS, ACT>(p, lds, c, tm * BM, tn * kTileCols, acc);
+    f32x4 acc[Tile<NXB>::XB][WB];
+    zero<NXB>(acc);
+    mainloop<NXB, kGated>(p, lds, c, tm * BM, tn * kTileCols, 0, p.K / BK, acc);
+    epilogue<NXB, OUT_BF16, HAS_BIAS, ACT>(p, lds, c, tm * BM, tn * kTileCols, acc);
 }
 
-template <int TM, bool OUT_BF16, bool HAS_BIAS, int ACT>
+template <int NXB, bool OUT_BF16, bool HAS_BIAS, int ACT>
 hipError_t launch_tm(GemmParams gp, hipStream_t stream)
 {
-    gp.tiles_m = (gp.M + Tile<TM>::BM - 1) / Tile<TM>::BM;
+    gp.tiles_m = (gp.M + Tile<NXB>::BM - 1) / Tile<NXB>::BM;
     gp.group_m = gp.tiles_m < 8 ? gp.tiles_m : 8;
-    hipLaunchKernelGGL((gemm_bf16_nt_kernel<TM, OUT_BF16, HAS_BIAS, ACT>), dim3(gp.tiles_m * gp.tiles_n),
+    hipLaunchKernelGGL((gemm_bf16_nt_kernel<NXB, OUT_BF16, HAS_BIAS, ACT>), dim3(gp.tiles_m * gp.tiles_n),
                        dim3(kThreads), 0, stream, gp);
     return hipGetLastError();
 }
 
 template <bool OUT_BF16, bool HAS_BIAS, int ACT>
-hipError_t launch_variant(const GemmParams &gp, int tm, hipStream_t stream)
+hipError_t launch_variant(const GemmParams &gp, int nxb, hipStream_t stream)
 {
-    return tm == 3 ? launch_tm<3, OUT_BF16, HAS_BIAS, ACT>(gp, stream)
-                   : launch_tm<4, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+    switch (nxb) {
+    case 6: return launch_tm<6, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+    case 7: return launch_tm<7, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+    default: return launch_tm<8, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+    }
 }
 
 // Compute units of the current device (cached per device).
@@ -422,16 +431,31 @@ int cu_count()
     return n;
 }
 
-// Tile height: the number of rounds of tiles over the CUs, times the tile's
-// share of a 256-row tile's work, with 5% added for the 192-row tile (5
-// fragment reads per 6 MFMAs instead of 6 per 8).
-int pick_tm(int M, int tiles_n, int cus)
+// Tile height: the one with the least cost = (rounds of tiles over the CUs)
+// x (tile rows) x (fragment-read overhead): a wave reads NXB + 4 fragments
+// per 4 NXB MFMAs, so shorter tiles read more per flop (measured about 5% for
+// 192 rows against 256).  Ties go to the taller tile.  224-row tiles are only
+// considered for K >= 3072: with a short k loop the per-tile start and store
+// outweighed the finer quantization (measured in the bench step, rowwise
+// 4608 x 6144: 4-6% faster at K = 4608 and 9216, 2-5% slower at K = 768-2304).
+int pick_nxb(int M, int tiles_n, int K, int cus)
 {
-    const int64_t t4 = (int64_t)((M + 255) / 256) * tiles_n;
-    const int64_t t3 = (int64_t)((M + 191) / 192) * tiles_n;
-    const double c4 = (double)((t4 + cus - 1) / cus);
-    const double c3 = (double)((t3 + cus - 1) / cus) * 0.75 * 1.05;
-    return c3 < c4 ? 3 : 4;
+    static const int kNxb[3] = {8, 7, 6};
+    static const double kOverhead[3] = {1.0, 1.025, 1.05};
+    int best = 8;
+    double best_cost = 0;
+    for (int i = 0; i < 3; ++i) {
+        if (kNxb[i] == 7 && K < 3072)
+            continue;
+        const int bm = 32 * kNxb[i];
+        const int64_t tiles = (int64_t)((M + bm - 1) / bm) * tiles_n;
+        const double cost = (double)((tiles + cus - 1) / cus) * bm * kOverhead[i];
+        if (i == 0 || cost < best_cost) {
+            best = kNxb[i];
+            best_cost = cost;
+        }
+    }
+    return best;
 }
 
 }  // namespace
@@ -452,22 +476,22 @@ hipError_t launch_gemm(const LinearProblem &pr, hipStream_t stream)
     const int act = pr.swiglu ? kActSwiglu : (pr.gelu ? kActGelu : kActNone);
     const int tile_cols = pr.swiglu ? BN / 2 : BN;
     gp.tiles_n = (int)((pr.N + tile_cols - 1) / tile_cols);
-    const int tm = pick_tm(gp.M, gp.tiles_n, cu_count());
+    const int nxb = pick_nxb(gp.M, gp.tiles_n, gp.K, cu_count());
     const bool bias = pr.bias != nullptr;
     const int sel = (pr.out_bf16 ? 6 : 0) + (bias ? 3 : 0);
     switch (sel + act) {
-    case 0: return launch_variant<false, false, 0>(gp, tm, stream);
-    case 1: return launch_variant<false, false, 1>(gp, tm, stream);
-    case 2: return launch_variant<false, false, 2>(gp, tm, stream);
-    case 3: return launch_variant<false, true, 0>(gp, tm, stream);
-    case 4: return launch_variant<false, true, 1>(gp, tm, stream);
-    case 5: return launch_variant<false, true, 2>(gp, tm, stream);
-    case 6: return launch_variant<true, false, 0>(gp, tm, stream);
-    case 7: return launch_variant<true, false, 1>(gp, tm, stream);
-    case 8: return launch_variant<true, false, 2>(gp, tm, stream);
-    case 9: return launch_variant<true, true, 0>(gp, tm, stream);
-    case 10: return launch_variant<true, true, 1>(gp, tm, stream);
-    default: return launch_variant<true, true, 2>(gp, tm, stream);
+    case 0: return launch_variant<false, false, 0>(gp, nxb, stream);
+    case 1: return launch_variant<false, false, 1>(gp, nxb, stream);
+    case 2: return launch_variant<false, false, 2>(gp, nxb, stream);
+    case 3: return launch_variant<false, true, 0>(gp, nxb, stream);
+    case 4: return launch_variant<false, true, 1>(gp, nxb, stream);
+    case 5: return launch_variant<false, true, 2>(gp, nxb, stream);
+    case 6: return launch_variant<true, false, 0>(gp, nxb, stream);
+    case 7: return launch_variant<true, false, 1>(gp, nxb, stream);
+    case 8: return launch_variant<true, false, 2>(gp, nxb, stream);
+    case 9: return launch_variant<true, true, 0>(gp, nxb, stream);
+    case 10: return launch_variant<true, true, 1>(gp, nxb, stream);
+    default: return launch_variant<true, true, 2>(gp, nxb, stream);
     }
 }
 

@@ -2,10 +2,14 @@
 weight-streaming kernel) against the oracle, through the C ABI.
 
 Ragged shapes span several tiles with partial tiles on both edges.  The
-kernel picks its tile height per shape (192 or 256 rows, whichever needs less
-time in rounds of tiles over the CUs): on a 256-CU device every RAGGED and
-LARGE shape fits in one round and runs 192-row tiles, and TALL runs 256-row
-tiles (432 of them in two rounds, against 576 of 192 rows in three).
+kernel picks its tile height per shape (192, 224 or 256 rows, whichever needs
+the least time in rounds of tiles over the CUs; 224 rows only for K >= 3072).
+On a 256-CU device every RAGGED and LARGE shape fits in one round and runs
+192-row tiles.  TALL runs 224-row tiles (504 in two rounds, against 432 of
+256 rows, also two rounds, or 576 of 192 rows in three), so its last tile row
+is ragged inside a tile whose last X DMA instruction is issued by half the
+waves.  WIDE runs 256-row tiles (256 in one round, against 352 of 192 rows in
+two).
 Integer-valued inputs make every summation order exact, so there the GPU must
 equal the oracle bit for bit, which pins operand layout and indexing; random
 inputs are held to the stated tolerance and to the derived per-element bound.
@@ -199,7 +203,7 @@ def test_large_repeat_runs_and_output_dtypes_agree():
     assert torch.equal(a.view(torch.int32), c.view(torch.int32))
 
 
-TALL = (4600, 6128, 128)
+TALL = (4600, 6128, 3072)
 
 
 def test_tall_integer_inputs_exact():
@@ -209,12 +213,40 @@ def test_tall_integer_inputs_exact():
     w = si.int_bf16(rng, (N, K), -4, 4)
     b = si.int_bf16(rng, (N,), -8, 8)
     y = tsl.tp_linear_colwise(bits_to_dev(x), bits_to_dev(w), bits_to_dev(b), out_dtype=torch.float32)
-    rows = np.unique(np.concatenate([np.arange(0, M, 211), [255, 256, M - 1]]))
+    rows = np.unique(np.concatenate([np.arange(0, M, 211), [223, 224, 255, 256, 4479, 4480, M - 1]]))
     assert np.array_equal(dev_to_f64(y)[rows], oracle.colwise(x, w, b, rows=rows))
     xi = torch.from_numpy(oracle.bf16_widen(x)).to(torch.float64)
     wi = torch.from_numpy(oracle.bf16_widen(w)).to(torch.float64)
     bi = torch.from_numpy(oracle.bf16_widen(b)).to(torch.float64)
     assert torch.equal(y.cpu().to(torch.float64), xi @ wi.T + bi)
+
+
+WIDE = (2040, 8176, 128)
+
+
+def test_wide_integer_inputs_exact():
+    M, N, K = WIDE
+    rng = np.random.default_rng(41)
+    x = si.int_bf16(rng, (M, K), -4, 4)
+    w = si.int_bf16(rng, (N, K), -4, 4)
+    p = tsl.tp_linear_rowwise(bits_to_dev(x), bits_to_dev(w))
+    xi = torch.from_numpy(oracle.bf16_widen(x)).to(torch.float64)
+    wi = torch.from_numpy(oracle.bf16_widen(w)).to(torch.float64)
+    assert torch.equal(p.cpu().to(torch.float64), xi @ wi.T)
+    rows = np.unique(np.concatenate([np.arange(0, M, 173), [255, 256, 1791, 1792, M - 1]]))
+    assert np.array_equal(dev_to_f64(p)[rows], oracle.linear(x, w, rows=rows))
+
+
+def test_wide_random_gelu_vs_oracle():
+    M, N, K = WIDE
+    rng = np.random.default_rng(43)
+    x = si.normal_bf16(rng, (M, K))
+    w = si.normal_bf16(rng, (N, K), 1 / np.sqrt(K))
+    b = si.normal_bf16(rng, (N,))
+    y = tsl.tp_linear_colwise(bits_to_dev(x), bits_to_dev(w), bits_to_dev(b), act="gelu_tanh")
+    rows = np.unique(np.concatenate([np.arange(0, M, 131), [255, 256, 1791, 1792, M - 1]]))
+    ref = oracle.colwise(x, w, b, act=oracle.ACT_GELU_TANH, rows=rows)
+    check_close(dev_to_f64(y)[rows], ref, K, True, S=abs_dot(x[rows], w, b), what="wide colwise gelu")
 
 
 def test_tall_random_gelu_vs_oracle():
@@ -224,7 +256,7 @@ def test_tall_random_gelu_vs_oracle():
     w = si.normal_bf16(rng, (N, K), 1 / np.sqrt(K))
     b = si.normal_bf16(rng, (N,))
     y = tsl.tp_linear_colwise(bits_to_dev(x), bits_to_dev(w), bits_to_dev(b), act="gelu_tanh")
-    rows = np.unique(np.concatenate([np.arange(0, M, 149), [255, 256, 4351, 4352, M - 1]]))
+    rows = np.unique(np.concatenate([np.arange(0, M, 149), [223, 224, 255, 256, 4351, 4352, 4479, 4480, M - 1]]))
     ref = oracle.colwise(x, w, b, act=oracle.ACT_GELU_TANH, rows=rows)
     check_close(dev_to_f64(y)[rows], ref, K, True, S=abs_dot(x[rows], w, b), what="tall colwise gelu")
 
