@@ -157,6 +157,32 @@ def test_skinny_path_integer_exact(B):
     assert np.array_equal(dev_to_f64(p), oracle.linear(c, w))
 
 
+@pytest.mark.parametrize("K", [6144, 5696])
+@pytest.mark.parametrize("B", [1, 2, 3, 4])
+def test_skinny_adaln_width_exact(B, K):
+    """The adaLN width: K in (4096, 6144] is 12 chunks per lane, and K = 5696
+    leaves lanes past the row end.  Integer inputs: exact, with bias."""
+    rng = np.random.default_rng(60 + B + K)
+    N = 400
+    c = si.int_bf16(rng, (B, K), -2, 2)
+    w = si.int_bf16(rng, (N, K), -2, 2)
+    b = si.int_bf16(rng, (N,), -8, 8)
+    y = tsl.tp_linear_colwise(bits_to_dev(c), bits_to_dev(w), bits_to_dev(b), out_dtype=torch.float32)
+    assert np.array_equal(dev_to_f64(y), oracle.colwise(c, w, b))
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 4])
+def test_skinny_adaln_width_random_gelu(B):
+    rng = np.random.default_rng(70 + B)
+    N, K = 528, 6144
+    c = si.normal_bf16(rng, (B, K))
+    w = si.normal_bf16(rng, (N, K), 1 / np.sqrt(K))
+    bb = si.normal_bf16(rng, (N,))
+    y = tsl.tp_linear_colwise(bits_to_dev(c), bits_to_dev(w), bits_to_dev(bb), act="gelu_tanh")
+    ref = oracle.colwise(c, w, bb, act=oracle.ACT_GELU_TANH)
+    check_close(dev_to_f64(y), ref, K, True, S=abs_dot(c, w, bb), what=f"skinny adaLN width B={B}")
+
+
 # Larger shapes: 1100 x 1040 x 2048 is ragged on both edges of a 5 x 5 tile
 # grid with 32 k-tiles; 4608 x 2304 x 3072 is a full-size rowwise shard.
 LARGE_SHAPES = [(1100, 1040, 2048), (4608, 2304, 3072)]
