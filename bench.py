@@ -743,8 +743,11 @@ def main():
     if args.detail:
         for k, s in sorted(shapes.items()):
             sec = s["ms"] * 1e-3
+            # roofline fraction: max(flops / MFMA peak, bytes / HBM peak) over the measured time
+            roof = max(s["flops"] / (PEAK_BF16_TFLOPS * 1e12), s["bytes"] / (PEAK_HBM_GBS * 1e9)) / sec
             print(f"# {k:48s} launches={s['launches']:4d} avg_us={s['ms'] * 1e3 / s['launches']:9.1f} "
-                  f"TFLOP/s={s['flops'] / sec / 1e12:8.1f} GB/s={s['bytes'] / sec / 1e9:8.1f}", file=sys.stderr)
+                  f"TFLOP/s={s['flops'] / sec / 1e12:8.1f} GB/s={s['bytes'] / sec / 1e9:8.1f} "
+                  f"roofline_frac={roof:.3f}", file=sys.stderr)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(result), flush=True)
