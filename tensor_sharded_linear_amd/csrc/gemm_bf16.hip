@@ -9,9 +9,10 @@
 // block of W and X with an fp32 store and no bias (the partial sum).
 //
 // Design for gfx950:
-//  * 256 x 256 output tile per workgroup, K step 64, 512 threads = 8 waves in
-//    a 2 (M) x 4 (N) grid; each wave owns a 128 x 64 sub-tile held as 8 x 4
-//    MFMA 16x16 fp32 accumulators (128 accumulator registers per lane).  Two
+//  * 256 x 256 output tile per workgroup (224 or 192 rows where that fills
+//    the CUs better), K step 64, 512 threads = 8 waves in a 2 (M) x 4 (N)
+//    grid; each wave owns a 128 x 64 sub-tile held as 8 x 4 MFMA 16x16 fp32
+//    accumulators (128 accumulator registers per lane).  Two
 //    waves per SIMD, so one wave's LDS fragment reads overlap the other's
 //    MFMAs; one wave per SIMD left the LDS read port idle half the time.
 //  * The part runs at its power limit on dense random operands (the same
@@ -31,7 +32,7 @@
 //    overwrites, so the DMA runs a whole k-tile ahead and no fragment read is
 //    exposed.
 //  * LDS tiles are 64-element (128-byte) rows; the 16-byte chunk c of row r
-//    is stored at position c ^ ((r >> 1) & 7).  A fragment read covers 32
+//    is stored at position c ^ ((r >> 1) & 7).  A fragment read covers
 //    16 rows of one chunk column per 16 lanes; under this swizzle each group
 //    of lanes that the LDS serves together touches distinct banks.
 //  * The W fragment is the MFMA "A" operand and the X fragment the "B"
