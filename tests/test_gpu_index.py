@@ -52,7 +52,9 @@ def test_packed_rowwise_slice_matches_column_view_of_packed_colwise():
         assert np.array_equal(dev_to_bits(ws), ref.T)
 
 
-@pytest.mark.parametrize("H,hd,K,P", [(24, 128, 3072, 4), (4, 2, 8, 2), (6, 8, 16, 3), (48, 128, 64, 8)])
+# (4, 2, 8, 4): one head per rank (P = H); (24, 128, 64, 1): P = 1 is the identity
+@pytest.mark.parametrize("H,hd,K,P", [(24, 128, 3072, 4), (4, 2, 8, 2), (6, 8, 16, 3), (48, 128, 64, 8),
+                                      (4, 2, 8, 4), (24, 128, 64, 1), (48, 128, 6144, 16)])
 def test_qkv_split_bit_exact_and_roundtrip(H, hd, K, P):
     w = _rand_bits(H * hd + K, (3 * H * hd, K))
     b = _rand_bits(H, (3 * H * hd,))
@@ -79,7 +81,8 @@ def test_qkv_split_rejects_head_count_not_divisible():
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("M,n_part,P,blocks", [(64, 512, 2, None), (7, 48, 4, [1, 1, 1]),
                                                (33, 8, 2, [1, 1]), (5, 18, 2, [1, 1, 1, 3, 3]),
-                                               (300, 2304, 8, [1, 1, 1]), (1, 4, 16, None)])
+                                               (300, 2304, 8, [1, 1, 1]), (1, 4, 16, None),
+                                               (16, 64, 1, None), (9, 6, 1, [1, 1, 1])])
 def test_concat_bit_exact(dtype, M, n_part, P, blocks):
     rng = np.random.default_rng(M * n_part + P)
     if dtype == torch.bfloat16:
