@@ -125,13 +125,18 @@ __device__ __forceinline__ void tile_of(int lin, const GemmParams &p, int &tm, i
 }
 
 // GELU, tanh form: g(v) = v/2 (1 + tanh(u)), u = sqrt(2/pi) (v + 0.044715 v^3).
-// Uses 1 + tanh(u) = 2 / (1 + exp(-2u)), so g(v) = v / (1 + exp(-2u)); both
-// tails are exact limits (exp -> inf gives -0, exp -> 0 gives v).
+// Uses 1 + tanh(u) = 2 / (1 + exp(-2u)), so g(v) = v / (1 + exp(-2u)), with
+// exp(-2u) = 2^(v (a + b v^2)), a = -2 sqrt(2/pi) log2(e), b = 0.044715 a.
+// The hardware exp2 and reciprocal (about 1 ulp each) replace the library
+// exp and the IEEE divide: 7 instructions per element instead of about 19,
+// which took 6% of a 4608 x 9216 x 6144 launch in the epilogue.  Both tails
+// are exact limits (2^+inf gives v * 0 = -0, 2^-inf gives v).
 __device__ __forceinline__ float gelu_tanh(float v)
 {
-    const float kSqrt2OverPi = 0.7978845608028654f;
-    const float u = kSqrt2OverPi * (v + 0.044715f * v * v * v);
-    return v / (1.0f + __expf(-2.0f * u));
+    const float a = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+    const float b = 0.044715f * a;
+    const float e = __builtin_amdgcn_exp2f(v * __builtin_fmaf(b, v * v, a));
+    return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // One k32 step's operand fragments: per lane 8 bf16 of one row of each of
@@ -285,9 +290,13 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
 #undef TPL_STEP
 }
 
-// SiLU (Swish): v * sigmoid(v) = v / (1 + exp(-v)); both tails are exact
-// limits (exp -> inf gives -0, exp -> 0 gives v).
-__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+// SiLU (Swish): v * sigmoid(v) = v / (1 + exp(-v)) = v / (1 + 2^(-v log2(e))),
+// with the hardware exp2 and reciprocal as in gelu_tanh; both tails are exact
+// limits (2^+inf gives -0, 2^-inf gives v).
+__device__ __forceinline__ float silu(float v)
+{
+    return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * -1.4426950408889634f));
+}
 
 // Epilogue activations.
 constexpr int kActNone = 0;

@@ -38,11 +38,15 @@ struct GemvParams {
     int M, N, K;
 };
 
+// GELU, tanh form, as in the tiled kernel: g(v) = v / (1 + exp(-2u)),
+// u = sqrt(2/pi) (v + 0.044715 v^3), with exp(-2u) = 2^(v (a + b v^2)) on the
+// hardware exp2 and the reciprocal.
 __device__ __forceinline__ float gelu_tanh(float v)
 {
-    const float kSqrt2OverPi = 0.7978845608028654f;
-    const float u = kSqrt2OverPi * (v + 0.044715f * v * v * v);
-    return v / (1.0f + __expf(-2.0f * u));
+    const float a = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+    const float b = 0.044715f * a;
+    const float e = __builtin_amdgcn_exp2f(v * __builtin_fmaf(b, v * v, a));
+    return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 __device__ __forceinline__ float dot8(const bf16x8 &a, const bf16x8 &b, float acc)
