@@ -41,12 +41,48 @@ template <> struct VecType<8> { typedef u32x2 T; };
 template <> struct VecType<4> { typedef uint32_t T; };
 template <> struct VecType<2> { typedef uint16_t T; };
 
+// Rows of at most kThreads / 2 vectors are short: a row-by-row sweep would
+// leave at least half of the workgroup idle.
+__host__ __device__ inline bool short_rows(int64_t nv) { return nv > 0 && nv <= kThreads / 2; }
+
+// Rows per block of the short-row sweep: kThreads / gcd(n, kThreads) for n
+// vectors per row (kThreads is a power of two), so that a block is a whole
+// number of passes of the workgroup.
+__host__ __device__ inline int short_row_block(int n)
+{
+    int tz = 0;
+    while (tz < 8 && ((n >> tz) & 1) == 0)
+        ++tz;
+    return kThreads >> tz;
+}
+
 template <int VEC, bool NT_STORE>
 __global__ __launch_bounds__(kThreads) void copy_segments_kernel(CopyArgs a)
 {
     typedef typename VecType<VEC>::T V;
     const CopySegment s = a.seg[blockIdx.y];
     const int64_t nv = s.row_bytes / VEC;
+    if (short_rows(nv)) {
+        // Short rows (the tp 8 pieces of a packed CONCAT, 1.5 KiB): the
+        // workgroup takes blocks of rb rows and sweeps each block's rb * nv
+        // vectors as one range.
+        const int n = (int)nv;
+        const int rb = short_row_block(n);
+        for (int64_t r0 = (int64_t)blockIdx.x * rb; r0 < s.rows; r0 += (int64_t)gridDim.x * rb) {
+            const int rows = (int)min((int64_t)rb, s.rows - r0);
+            for (int f = threadIdx.x; f < rows * n; f += kThreads) {
+                const int q = f / n;
+                const int v = f - q * n;
+                const V t = __builtin_nontemporal_load(reinterpret_cast<const V *>(s.src + (r0 + q) * s.src_ld) + v);
+                V *dst = reinterpret_cast<V *>(s.dst + (r0 + q) * s.dst_ld) + v;
+                if (NT_STORE)
+                    __builtin_nontemporal_store(t, dst);
+                else
+                    *dst = t;
+            }
+        }
+        return;
+    }
     for (int64_t r = blockIdx.x; r < s.rows; r += gridDim.x) {
         const V *src = reinterpret_cast<const V *>(s.src + r * s.src_ld);
         V *dst = reinterpret_cast<V *>(s.dst + r * s.dst_ld);
@@ -68,7 +104,6 @@ hipError_t launch_copy_segments(const CopySegment *segs, int nseg, hipStream_t s
         const int cnt = nseg - base < kMaxSegmentsPerLaunch ? nseg - base : kMaxSegmentsPerLaunch;
         CopyArgs a;
         uint64_t bits = 0;
-        int64_t max_rows = 0;
         bool contiguous_dst = true;  // every destination one contiguous range
         for (int i = 0; i < cnt; ++i) {
             const CopySegment &s = segs[base + i];
@@ -76,16 +111,28 @@ hipError_t launch_copy_segments(const CopySegment *segs, int nseg, hipStream_t s
             contiguous_dst = contiguous_dst && (s.rows <= 1 || s.dst_ld == s.row_bytes);
             bits |= (uint64_t)(uintptr_t)s.src | (uint64_t)(uintptr_t)s.dst | (uint64_t)s.src_ld |
                     (uint64_t)s.dst_ld | (uint64_t)s.row_bytes;
-            if (s.rows > max_rows)
-                max_rows = s.rows;
         }
-        if (max_rows == 0)
+        const int vec = (bits & 15) == 0 ? 16 : (bits & 7) == 0 ? 8 : (bits & 3) == 0 ? 4 : 2;
+        // Workgroups per segment: one per row, or one per block of short rows;
+        // the largest count over the segments, capped so that the grid still
+        // covers the chip several times.
+        int64_t max_groups = 0;
+        for (int i = 0; i < cnt; ++i) {
+            const CopySegment &s = segs[base + i];
+            const int64_t nv = s.row_bytes / vec;
+            int64_t groups = nv > 0 ? s.rows : 0;
+            if (short_rows(nv)) {
+                const int rb = short_row_block((int)nv);
+                groups = (s.rows + rb - 1) / rb;
+            }
+            if (groups > max_groups)
+                max_groups = groups;
+        }
+        if (max_groups == 0)
             continue;
-        // Rows per segment: enough workgroups to cover the chip several times.
-        int64_t gx = max_rows < 4096 ? max_rows : 4096;
+        int64_t gx = max_groups < 4096 ? max_groups : 4096;
         const dim3 grid((unsigned)gx, (unsigned)cnt);
         const dim3 block(kThreads);
-        const int vec = (bits & 15) == 0 ? 16 : (bits & 7) == 0 ? 8 : (bits & 3) == 0 ? 4 : 2;
         switch (vec * 2 + (contiguous_dst ? 1 : 0)) {
         case 33: hipLaunchKernelGGL((copy_segments_kernel<16, true>), grid, block, 0, stream, a); break;
         case 32: hipLaunchKernelGGL((copy_segments_kernel<16, false>), grid, block, 0, stream, a); break;
