@@ -341,12 +341,66 @@ def reduce_traffic(fetch_dir, write_dir, probe_json):
     print(json.dumps(out))
 
 
+class TimingEvent:
+    """A HIP event used only to time GPU work, created with hipEventDisableSystemFence.
+
+    A default event record ends with a system-scope release: the L2 is written back and
+    invalidated.  Between two kernels that costs about 5 us of idle GPU per record, and the next
+    kernel restarts from cold caches.  Timing needs neither: the timestamps are read only after
+    a device synchronize.  The event lives in the HIP runtime that torch loaded, so torch's
+    stream handles are valid for it.
+    """
+
+    _hip = None
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            lib = ctypes.CDLL("libamdhip64.so.7")  # the copy torch already loaded (same soname)
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            for fn in (lib.hipEventCreateWithFlags, lib.hipEventRecord, lib.hipEventElapsedTime, lib.hipEventDestroy):
+                fn.restype = ctypes.c_int
+            cls._hip = lib
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._ct = ctypes
+        self.h = ctypes.c_void_p()
+        self._check(self._lib().hipEventCreateWithFlags(ctypes.byref(self.h), self.FLAGS), "hipEventCreateWithFlags")
+
+    @staticmethod
+    def _check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def record(self, stream):
+        self._check(self._lib().hipEventRecord(self.h, self._ct.c_void_p(stream.cuda_stream)), "hipEventRecord")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end`; call after a device synchronize."""
+        ms = self._ct.c_float()
+        self._check(self._lib().hipEventElapsedTime(self._ct.byref(ms), self.h, end.h), "hipEventElapsedTime")
+        return ms.value
+
+    def destroy(self):
+        if self.h:
+            self._check(self._lib().hipEventDestroy(self.h), "hipEventDestroy")
+            self.h = self._ct.c_void_p()
+
+
 class Timer:
     """HIP events over the timed launches, on the stream each launch runs on.
 
     By default consecutive launches of one kernel family on one stream share
     one event pair, so the events add no gaps between them; a family's
-    average launch time is the summed group time over its launch count.
+    average launch time is the summed group time over its launch count.  The
+    event that closes one group opens the next one on the same stream.
     With per_launch=True every launch gets its own pair (per-shape detail).
     """
 
@@ -358,11 +412,14 @@ class Timer:
         self.open = {}   # stream -> [category, items, ev0]
 
     def _close(self, s):
+        """Ends the open group on stream s; returns the event that ended it (or None)."""
         g = self.open.pop(s, None)
-        if g is not None:
-            e1 = self.torch.cuda.Event(enable_timing=True)
-            e1.record(s)
-            self.rec.append((g[0], g[1], g[2], e1))
+        if g is None:
+            return None
+        e1 = TimingEvent()
+        e1.record(s)
+        self.rec.append((g[0], g[1], g[2], e1))
+        return e1
 
     def run(self, cat, key, flops, nbytes, fn, stream=None):
         """Launch fn on `stream` (torch's current stream if None), timed by events on it."""
@@ -372,9 +429,12 @@ class Timer:
                 return fn()
             g = self.open.get(s)
             if self.per_launch or g is None or g[0] != cat:
-                self._close(s)
-                e0 = self.torch.cuda.Event(enable_timing=True)
-                e0.record(s)
+                # Where one group follows another on the stream, the event that ends the first
+                # also starts the second: one record per change of family.
+                e0 = self._close(s)
+                if e0 is None or self.per_launch:
+                    e0 = TimingEvent()
+                    e0.record(s)
                 g = self.open[s] = [cat, [], e0]
             out = fn()
             g[1].append((key, flops, nbytes))
@@ -389,6 +449,7 @@ class Timer:
                 self._close(s)
 
     def summary(self):
+        """Per-family and per-shape totals; call once, after a device synchronize."""
         cats = {}
         shapes = {}
         for cat, items, e0, e1 in self.rec:
@@ -406,6 +467,13 @@ class Timer:
                 sh["flops"] += flops
                 sh["bytes"] += nbytes
                 sh["launches"] += 1
+        # The timestamps are read; the events are released (the records stay for their keys).
+        done = set()
+        for r in self.rec:
+            for e in (r[2], r[3]):
+                if id(e) not in done:
+                    done.add(id(e))
+                    e.destroy()
         return cats, shapes
 
 

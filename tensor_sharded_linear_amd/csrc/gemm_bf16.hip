@@ -42,7 +42,8 @@
 //    whole row segments (4 rows x 256 B fp32, 8 rows x 128 B bf16 per
 //    instruction): direct stores from the MFMA layout cover 16 rows x 16 B
 //    per instruction and wrote 1.64x the algorithmic bytes for an fp32
-//    output when measured with the 32x32 layout.
+//    output when measured with the 32x32 layout.  The stores are
+//    non-temporal.
 //  * Workgroups are dealt round-robin to the 8 XCDs; the tile index is
 //    remapped so each XCD gets a contiguous run of a grouped raster order,
 //    which keeps its concurrent tiles on few X row-panels and W row-panels
@@ -370,8 +371,10 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, con
             const int row = r + rd_row;
             const int m = mbase + row;
             const f32x4 v = *reinterpret_cast<const f32x4 *>(stage + row * kRowElems + rd_vec * kVec);
+            // Non-temporal stores: about 1% faster than ordinary ones over a DiT block's
+            // GEMMs, with the same fetched and written bytes.
             if (m < p.M && ncol0 < p.N)
-                *reinterpret_cast<f32x4 *>(reinterpret_cast<OutT *>(p.y) + (int64_t)m * p.ldy + ncol0) = v;
+                __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(reinterpret_cast<OutT *>(p.y) + (int64_t)m * p.ldy + ncol0));
         }
     }
 }
