@@ -59,10 +59,15 @@ def parse():
     ap.add_argument("--streams", type=int, default=1, choices=(1, 2),
                     help="2: slicing and combines on a second stream beside the GEMMs (measured slower)")
     ap.add_argument("--probe", metavar="OUT_JSON",
-                    help="untimed: two steps, then a calibration copy of known size, for rocprofv3 --pmc "
-                         "FETCH_SIZE / WRITE_SIZE runs; writes the step's algorithmic GEMM bytes to OUT_JSON")
-    ap.add_argument("--traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PROBE_JSON"),
-                    help="no GPU: reduce the two counter runs of --probe to " + os.path.relpath(TRAFFIC_FILE, ROOT))
+                    help="untimed: two steps, then a calibration copy of known size, for rocprofv3 --pmc runs; "
+                         "writes the second step's launch list (family, shape, flops, algorithmic bytes) to "
+                         "OUT_JSON")
+    ap.add_argument("--cold-md", metavar="OUT_MD",
+                    help="also write the cold per-call table of the HBM-bound calls to OUT_MD")
+    ap.add_argument("--counters", nargs="+", metavar="PATH",
+                    help="no GPU: PROBE_JSON RUN_DIR [RUN_DIR ...]: join rocprofv3 --pmc runs of --probe with its "
+                         "launch list; writes profiles/dit_block_step_counters.md and, from FETCH_SIZE and "
+                         "WRITE_SIZE runs, " + os.path.relpath(TRAFFIC_FILE, ROOT))
     ap.add_argument("--load", action="store_true",
                     help="checkpoint-load benchmark instead of the step: the full block's weights in a synthetic "
                          "safetensors file, every rank of --load-tp loaded by tp_load_shard (shard as read) and "
@@ -264,81 +269,161 @@ def load_bench(args):
 CAL_ROWS, CAL_COLS = 8192, 8192   # calibration copy: a 128 MiB bf16 weight, copied whole (colwise, P = 1)
 
 
-def _counter_rows(d):
-    """Per-dispatch counter values of a rocprofv3 --pmc CSV run: [(dispatch, kernel, value)]."""
+KERNEL_OF = {"gemm": "gemm_bf16_nt_kernel", "gemv": "gemv_bf16_kernel", "sum": "combine_sum_kernel",
+             "slice": "copy_segments_kernel", "concat": "copy_segments_kernel"}
+N_XCC = 8          # GRBM_GUI_ACTIVE is counted per XCD; the CSV value is their sum
+SIMDS = 1024       # 256 CUs x 4 SIMDs
+
+
+def _dispatches(d):
+    """{dispatch id: [kernel name, {counter: value}, duration ns or None]} of one rocprofv3 run
+    directory (--pmc CSV output, with or without a kernel trace)."""
     import csv
     import glob
-    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
-    if len(files) != 1:
-        raise SystemExit(f"expected one counter_collection.csv under {d}, found {files}")
     out = {}
-    with open(files[0]) as f:
-        for r in csv.DictReader(f):
-            key = int(r["Dispatch_Id"])
-            out[key] = (r["Kernel_Name"], out.get(key, (None, 0.0))[1] + float(r["Counter_Value"]))
-    return [(k, n, v) for k, (n, v) in sorted(out.items())]
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                e = out.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], {}, None])
+                name = r["Counter_Name"]
+                e[1][name] = e[1].get(name, 0.0) + float(r["Counter_Value"])
+                if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                    e[2] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                k = int(r["Dispatch_Id"])
+                if k in out:
+                    out[k][2] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    if not out:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return out
 
 
-def reduce_traffic(fetch_dir, write_dir, probe_json):
-    """HBM bytes per GEMM launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
-    scaled by what the same counter reads for the calibration copy (CAL bytes read and
-    written), averaged over the GEMM launches of the probe's last step."""
+def reduce_counters(probe_json, dirs):
+    """Joins rocprofv3 --pmc runs of `bench.py --probe` with the probe's launch list.
+
+    Each run's last len(launches) + 1 dispatches of this library's kernels are the probe's
+    second step and the calibration copy (a copy of known size: CAL bytes read and the same
+    written).  FETCH_SIZE and WRITE_SIZE are scaled by what they read for that copy; MfmaUtil
+    (rocprofv3's derived metric: MFMA-busy cycles over GUI-active cycles x SIMDs), MfmaFlopsBF16
+    and GRBM_GUI_ACTIVE are taken as they are.  Writes profiles/gemm_traffic.json (the GEMM
+    family's HBM bytes per launch, read by the bench line) when both byte counters are there, and
+    profiles/dit_block_step_counters.md with the per-family and per-GEMM-shape tables."""
     with open(probe_json) as f:
         probe = json.load(f)
-    res = {}
-    for name, d in (("fetch", fetch_dir), ("write", write_dir)):
-        rows = _counter_rows(d)
-        gemm = [v for _, n, v in rows if "gemm_bf16_nt_kernel" in n]
-        cal = [v for _, n, v in rows if "copy_segments_kernel" in n][-1]
-        last = gemm[-probe["gemm_launches_per_step"]:]
-        factor = probe["cal_bytes"] / (cal * 1024.0)
-        res[name] = dict(kib_per_launch=sum(last) / len(last), calibration_kib=cal, factor=factor,
-                         bytes_per_launch=sum(last) / len(last) * 1024.0 * factor)
-    total = res["fetch"]["bytes_per_launch"] + res["write"]["bytes_per_launch"]
-    out = {
-        "kernel": "gemm_bf16_nt_kernel",
-        "source_sha": file_sha(GEMM_SRC),
-        "bytes_per_launch": round(total),
-        "algorithmic_bytes_per_launch": round(probe["alg_bytes_per_launch"]),
-        "ratio_to_algorithmic": round(total / probe["alg_bytes_per_launch"], 4),
-        "fetch": res["fetch"], "write": res["write"],
-        "calibration": f"copy_segments_kernel copying a {CAL_ROWS}x{CAL_COLS} bf16 weight: "
-                       f"{probe['cal_bytes']} bytes read and the same written",
-        "launches_averaged": probe["gemm_launches_per_step"],
-    }
-    with open(TRAFFIC_FILE, "w") as f:
-        json.dump(out, f, indent=1)
-    fe, wr = res["fetch"], res["write"]
-    alg_w = wr["bytes_per_launch"]  # measured writes: equal to the output bytes on these shapes
-    md = [
-        f"# HBM-side traffic of gemm_bf16_nt_kernel over one bench step ({probe['gemm_launches_per_step']} "
-        "GEMM launches)", "",
-        "Commands (run from the repository root on one MI355X; each counter in its own run):", "", "```",
-        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/tr_fetch -o run -- "
-        "python3 bench.py --probe gpurun_out/probe_f.json",
-        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/tr_write -o run -- "
-        "python3 bench.py --probe gpurun_out/probe.json",
-        "python3 bench.py --traffic gpurun_out/tr_fetch gpurun_out/tr_write gpurun_out/probe.json",
-        "```", "",
-        f"`--probe` runs two bench steps untimed, then one `copy_segments_kernel` copy of a {CAL_ROWS} x "
-        f"{CAL_COLS} bf16 weight ({probe['cal_bytes']} bytes read, the same written) as the calibration of "
-        "known size.  The figures are for the GEMM source with hash "
-        f"`{out['source_sha']}`.", "",
-        "| counter | calibration copy reads | factor | GEMM, per launch (last step) | scaled |",
-        "|---|---|---|---|---|",
-        f"| FETCH_SIZE | {fe['calibration_kib']:.0f} KiB (true {probe['cal_bytes'] / 1024:.0f} KiB) | "
-        f"{fe['factor']:.4f} | {fe['kib_per_launch']:.0f} KiB | {fe['bytes_per_launch'] / 1e6:.1f} MB |",
-        f"| WRITE_SIZE | {wr['calibration_kib']:.0f} KiB (true {probe['cal_bytes'] / 1024:.0f} KiB) | "
-        f"{wr['factor']:.4f} | {wr['kib_per_launch']:.0f} KiB | {wr['bytes_per_launch'] / 1e6:.1f} MB |", "",
-        f"Traffic {total / 1e6:.1f} MB per launch against {probe['alg_bytes_per_launch'] / 1e6:.1f} MB "
-        f"algorithmic (X and W read once, Y written once): {total / probe['alg_bytes_per_launch']:.2f}x.  "
-        f"Operand reads are {fe['bytes_per_launch'] / (probe['alg_bytes_per_launch'] - alg_w):.2f}x the "
-        "operand bytes, taking the writes as the output bytes: each XCD's L2 fetches every X and W panel "
-        "that its concurrent tiles touch.",
-    ]
-    with open(os.path.join(ROOT, "profiles", "gemm_traffic.md"), "w") as f:
+    launches = probe["launches"]
+    n = len(launches)
+    per = [dict() for _ in range(n)]       # counter -> value, per launch
+    dur = [[] for _ in range(n)]           # durations (ns) seen for the launch across runs
+    scale = {}
+    runs = []
+    for d in dirs:
+        disp = _dispatches(d)
+        ours = [(k, v) for k, v in sorted(disp.items()) if any(kn in v[0] for kn in set(KERNEL_OF.values()))]
+        if len(ours) < n + 1:
+            raise SystemExit(f"{d}: {len(ours)} library dispatches, fewer than the probe's {n} + 1")
+        step, cal = ours[-(n + 1):-1], ours[-1][1]
+        if "copy_segments_kernel" not in cal[0]:
+            raise SystemExit(f"{d}: the last dispatch is {cal[0]}, not the calibration copy")
+        for i, ((_, (name, cnt, ns)), (cat, key, _, _)) in enumerate(zip(step, launches)):
+            if KERNEL_OF[cat] not in name:
+                raise SystemExit(f"{d}: dispatch {i} is {name}, the probe says {cat} {key}")
+            for c, v in cnt.items():
+                per[i][c] = v
+            if ns:
+                dur[i].append(ns)
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            if c in cal[1]:
+                scale[c] = probe["cal_bytes"] / (cal[1][c] * 1024.0)
+                scale[c + "_cal_kib"] = cal[1][c]
+        runs.append(f"{d}: {', '.join(sorted(step[0][1][1]))}")
+
+    def mean(xs):
+        return sum(xs) / len(xs) if xs else float("nan")
+
+    # per family: counter bytes against algorithmic bytes
+    fam = {}
+    for i, (cat, key, flops, nbytes) in enumerate(launches):
+        e = fam.setdefault(cat, dict(n=0, alg=0.0, fetch=0.0, write=0.0))
+        e["n"] += 1
+        e["alg"] += nbytes
+        e["fetch"] += per[i].get("FETCH_SIZE", float("nan")) * 1024.0 * scale.get("FETCH_SIZE", float("nan"))
+        e["write"] += per[i].get("WRITE_SIZE", float("nan")) * 1024.0 * scale.get("WRITE_SIZE", float("nan"))
+    # per shape: everything averaged over the shape's launches
+    shp = {}
+    for i, (cat, key, flops, nbytes) in enumerate(launches):
+        e = shp.setdefault((cat, key), dict(n=0, flops=flops, alg=nbytes, rows=[]))
+        e["n"] += 1
+        e["rows"].append(i)
+    md = ["# Hardware counters of one bench step, per kernel family and per GEMM shape", "",
+          "Commands (run from the repository root on one MI355X; one counter set per run):", "", "```"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE", "MfmaUtil MfmaFlopsBF16 GRBM_GUI_ACTIVE"):
+        tag = c.split()[0].lower()
+        md.append(f"rocprofv3 --pmc {c} --kernel-trace --output-format csv -d gpurun_out/pmc_{tag} -o run -- "
+                  f"python3 bench.py --probe gpurun_out/probe_{tag}.json")
+    md += ["python3 bench.py --counters gpurun_out/probe_fetch_size.json gpurun_out/pmc_fetch_size "
+           "gpurun_out/pmc_write_size gpurun_out/pmc_mfmautil", "```", "",
+           f"`--probe` runs two bench steps untimed, then one copy of a {CAL_ROWS} x {CAL_COLS} bf16 weight "
+           f"({probe['cal_bytes']} bytes read, the same written) whose counters calibrate the byte counts.  "
+           f"The tables cover the {n} launches of the second step.  Under counter collection every dispatch "
+           "runs alone, so durations here are longer than in the timed bench, and the caches hold what the "
+           "step's previous kernel left, as in the bench.", "",
+           "Runs: " + "; ".join(runs), ""]
+    if "FETCH_SIZE" in scale and "WRITE_SIZE" in scale:
+        md += [f"Calibration: FETCH_SIZE read {scale['FETCH_SIZE_cal_kib']:.0f} KiB and WRITE_SIZE "
+               f"{scale['WRITE_SIZE_cal_kib']:.0f} KiB for {probe['cal_bytes'] / 1024:.0f} KiB moved each way: "
+               f"factors {scale['FETCH_SIZE']:.4f} and {scale['WRITE_SIZE']:.4f}.", "",
+               "## HBM traffic per family (counter bytes against algorithmic bytes)", "",
+               "| family | launches | algorithmic MB / launch | fetched MB / launch | written MB / launch | "
+               "traffic / algorithmic |", "|---|---|---|---|---|---|"]
+        for cat, e in sorted(fam.items()):
+            md.append(f"| {cat} | {e['n']} | {e['alg'] / e['n'] / 1e6:.1f} | {e['fetch'] / e['n'] / 1e6:.1f} | "
+                      f"{e['write'] / e['n'] / 1e6:.1f} | {(e['fetch'] + e['write']) / e['alg']:.3f} |")
+        md += ["", "Per shape:", "", "| family: shape | launches | algorithmic MB | fetched MB | written MB | ratio |",
+               "|---|---|---|---|---|---|"]
+        for (cat, key), e in sorted(shp.items()):
+            fe = mean([per[i].get("FETCH_SIZE", float("nan")) for i in e["rows"]]) * 1024 * scale["FETCH_SIZE"]
+            wr = mean([per[i].get("WRITE_SIZE", float("nan")) for i in e["rows"]]) * 1024 * scale["WRITE_SIZE"]
+            md.append(f"| {cat}: {key} | {e['n']} | {e['alg'] / 1e6:.1f} | {fe / 1e6:.1f} | {wr / 1e6:.1f} | "
+                      f"{(fe + wr) / e['alg']:.3f} |")
+        g = fam["gemm"]
+        out = {
+            "kernel": "gemm_bf16_nt_kernel", "source_sha": file_sha(GEMM_SRC),
+            "bytes_per_launch": round((g["fetch"] + g["write"]) / g["n"]),
+            "algorithmic_bytes_per_launch": round(g["alg"] / g["n"]),
+            "ratio_to_algorithmic": round((g["fetch"] + g["write"]) / g["alg"], 4),
+            "fetch_bytes_per_launch": round(g["fetch"] / g["n"]), "write_bytes_per_launch": round(g["write"] / g["n"]),
+            "factors": {"FETCH_SIZE": scale["FETCH_SIZE"], "WRITE_SIZE": scale["WRITE_SIZE"]},
+            "launches_averaged": g["n"],
+        }
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(out, f, indent=1)
+        print(json.dumps(out))
+    if any("MfmaUtil" in p for p in per):
+        md += ["", "## MFMA utilisation per GEMM shape", "",
+               "MfmaUtil is rocprofv3's derived metric: MFMA-busy cycles summed over the SIMDs, over "
+               "GUI-active cycles x 1024 SIMDs.  MFMA flops are MfmaFlopsBF16 (512 x the bf16 MFMA "
+               "math-op count); against the algorithmic 2MNK they show the work of the tiles' padding rows.  "
+               "The clock is GUI-active cycles (per XCD) over the dispatch's duration.", "",
+               "| shape | launches | µs (alone) | TFLOP/s (alone) | MfmaUtil % | MFMA flops / 2MNK | clock GHz | "
+               "MFMA flops per GUI cycle, % of 1024 x 1024 |", "|---|---|---|---|---|---|---|---|"]
+        tot = dict(busy=0.0, n=0)
+        for (cat, key), e in sorted(shp.items()):
+            if cat != "gemm":
+                continue
+            util = mean([per[i].get("MfmaUtil", float("nan")) for i in e["rows"]])
+            mf = mean([per[i].get("MfmaFlopsBF16", float("nan")) for i in e["rows"]])
+            gui = mean([per[i].get("GRBM_GUI_ACTIVE", float("nan")) for i in e["rows"]]) / N_XCC
+            us = mean([x for i in e["rows"] for x in dur[i]]) / 1e3
+            md.append(f"| {key} | {e['n']} | {us:.1f} | {e['flops'] / us / 1e6:.0f} | {util:.1f} | "
+                      f"{mf / e['flops']:.4f} | {gui / us / 1e3:.2f} | {100 * mf / gui / (SIMDS * 1024):.1f} |")
+            tot["busy"] += util * e["n"]
+            tot["n"] += e["n"]
+        md += ["", f"Launch-weighted MfmaUtil over the step's {tot['n']} GEMM launches: "
+                   f"{tot['busy'] / tot['n']:.1f}%."]
+    with open(os.path.join(ROOT, "profiles", "dit_block_step_counters.md"), "w") as f:
         f.write("\n".join(md) + "\n")
-    print(json.dumps(out))
 
 
 class TimingEvent:
@@ -484,8 +569,10 @@ def file_sha(path):
 
 def main():
     args = parse()
-    if args.traffic:
-        reduce_traffic(*args.traffic)
+    if args.counters:
+        if len(args.counters) < 2:
+            raise SystemExit("--counters needs PROBE_JSON and at least one run directory")
+        reduce_counters(args.counters[0], args.counters[1:])
         return
     if args.load_child:
         m, tp, path, out = args.load_child
@@ -711,14 +798,16 @@ def main():
         step()
         torch.cuda.synchronize()
         T.on = False
-        g = [it for r in T.rec if r[0] == "gemm" for it in r[1]]
+        launches = [[r[0], key, flops, nbytes] for r in T.rec for key, flops, nbytes in r[1]]
+        g = [it for it in launches if it[0] == "gemm"]
         cal = torch.empty(CAL_ROWS, CAL_COLS, dtype=torch.bfloat16, device=dev)
         tsl.tp_plan_shard_slice(cal, None, "colwise", 1, 0)
         torch.cuda.synchronize()
         with open(args.probe, "w") as f:
-            json.dump(dict(gemm_launches_per_step=len(g), alg_bytes_per_launch=sum(it[2] for it in g) / len(g),
+            json.dump(dict(launches=launches, gemm_launches_per_step=len(g),
+                           alg_bytes_per_launch=sum(it[3] for it in g) / len(g),
                            cal_bytes=2 * CAL_ROWS * CAL_COLS), f)
-        print(f"probe: {len(g)} GEMM launches per step", flush=True)
+        print(f"probe: {len(launches)} launches per step, {len(g)} of them GEMMs", flush=True)
         return
 
     for _ in range(args.warmup):
@@ -752,6 +841,105 @@ def main():
         gemv_rows[str(nb)] = dict(avg_us=round(c["ms"] * 1e3 / c["launches"], 2),
                                   gbs=round(c["bytes"] / (c["ms"] * 1e-3) / 1e9, 1),
                                   pct_hbm_peak=round(100 * c["bytes"] / (c["ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 1))
+
+    # Outside the step: every HBM-bound call of the step once per shape (rank 0), cold: a
+    # 512 MiB read evicts the 256 MB Infinity Cache before each call, and the call is timed
+    # alone by an event pair on its stream (median of 5).  Family figures weight each call by
+    # how often the step makes it.
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def cold_us(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(reps):
+            flush.sum()
+            e0, e1 = TimingEvent(), TimingEvent()
+            e0.record(ms)
+            fn()
+            e1.record(ms)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        for a, b in evs:
+            a.destroy()
+            b.destroy()
+        return ts[len(ts) // 2]
+
+    cold_calls = []   # (family, key, bytes, times per step, fn)
+    for P in tps:
+        b = bufs[P]
+        kq = 3 * H // P * hd
+        cold_calls += [
+            ("slice", f"qkv P{P}", 2 * 2 * kq * hidden, P,
+             lambda b=b, P=P: tsl.tp_fused_qkv_split(wqkv, None, H, hd, P, 0, w_out=b["wq"][0])),
+            ("slice", f"wo P{P}", 2 * 2 * hidden * hidden // P, P,
+             lambda b=b, P=P: tsl.tp_plan_shard_slice(wo, None, "rowwise", P, 0, w_out=b["wo"][0])),
+            ("slice", f"w1 P{P}", 2 * 2 * ffn // P * hidden, P,
+             lambda b=b, P=P: tsl.tp_plan_shard_slice(w1, None, "colwise", P, 0, w_out=b["w1"][0])),
+            ("slice", f"w2 P{P}", 2 * 2 * hidden * ffn // P, P,
+             lambda b=b, P=P: tsl.tp_plan_shard_slice(w2, None, "rowwise", P, 0, w_out=b["w2"][0])),
+            ("sum", f"P{P} f32", (P + 1) * 4.0 * M * hidden, 1,
+             lambda b=b: tsl.tp_partial_combine(b["po"], "sum", out=b["out_sum"])),
+            ("sum", f"P{P} bf16", (P * 4.0 + 2.0) * M * hidden, 1,
+             lambda b=b: tsl.tp_partial_combine(b["pd"], "sum", out=b["down_sum"])),
+            ("concat", f"qkv P{P}", 2 * 2.0 * M * 3 * H * hd, 1,
+             lambda b=b: tsl.tp_partial_combine(b["q"], "concat", blocks=[1, 1, 1], out=b["q_cat"])),
+            ("concat", f"up P{P}", 2 * 2.0 * M * ffn, 1,
+             lambda b=b: tsl.tp_partial_combine(b["h"], "concat", out=b["h_cat"])),
+        ]
+    cold_calls += [
+        ("slice", "w_gu [1,1]", 2 * 2 * 2 * n_gu * hidden, P_GU,
+         lambda: tsl.tp_plan_shard_slice(w_gu, b_gu, "colwise", P_GU, 0, blocks=[1, 1], w_out=gu_w[0],
+                                         b_out=gu_b[0])),
+        ("slice", "w_ada", 2 * 2 * n_ada * hidden, P_ADA,
+         lambda: tsl.tp_plan_shard_slice(w_ada, None, "colwise", P_ADA, 0, w_out=ada_w[0])),
+        ("slice", "w_ada split", 2 * 2 * n_full_ada * k_ada, P_ADA,
+         lambda: tsl.tp_plan_shard_slice(w_ada, None, "rowwise_split_input", P_ADA, 0, w_out=ada_ws[0])),
+        ("gemv", f"adaLN split-input B{B_ADA}", 2.0 * n_full_ada * k_ada + 2.0 * B_ADA * k_ada
+         + 4.0 * B_ADA * n_full_ada, P_ADA,
+         lambda: tsl.tp_linear_rowwise_split_input(c_ada, ada_ws[0], P_ADA, 0, out=ada_p[0])),
+    ]
+    for nb in range(1, B_ADA + 1):
+        yb = torch.empty(nb, n_ada, dtype=torch.bfloat16, device=dev)
+        cold_calls.append(("gemv", f"adaLN B{nb}", 2.0 * n_ada * hidden + 2.0 * nb * (hidden + n_ada),
+                           P_ADA if nb == B_ADA else 0,
+                           lambda nb=nb, yb=yb: tsl.tp_linear_colwise(c_ada[:nb], ada_w[0], out=yb)))
+    cold_rows = []
+    for fam, key, nbytes, mult, fn in cold_calls:
+        us = cold_us(fn)
+        cold_rows.append((fam, key, nbytes, mult, us))
+    del flush
+    cold_fam = {}
+    for fam, key, nbytes, mult, us in cold_rows:
+        if mult:
+            e = cold_fam.setdefault(fam, [0.0, 0.0])
+            e[0] += mult * nbytes
+            e[1] += mult * us * 1e-6
+    cold = {fam: dict(gbs=round(bb / t / 1e9, 1), pct_hbm_peak=round(100 * bb / t / 1e9 / PEAK_HBM_GBS, 1))
+            for fam, (bb, t) in sorted(cold_fam.items())}
+    cold["gemv_by_rows"] = {key.split("B")[-1]: round(100 * nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 1)
+                            for fam, key, nbytes, mult, us in cold_rows if key.startswith("adaLN B")}
+    if args.cold_md:
+        md = ["# Cold per-call times of the step's HBM-bound calls", "",
+              "Command (run from the repository root on one MI355X):", "", "```",
+              f"python3 bench.py --cold-md {args.cold_md}", "```", "",
+              "After the timed steps, each call below runs once per shape (rank 0) right after a 512 MiB read "
+              "that evicts the 256 MB Infinity Cache, timed alone by an event pair on its stream; the figure "
+              "is the median of 5.  GB/s is algorithmic bytes (read + write of a copy; every part plus the "
+              "output for a SUM; the weight plus activations and outputs for a GEMV) over that time.  The "
+              "family lines weight each call by how often one step makes it.", "",
+              "| family | call | MB | per step | µs | GB/s | % of 8 TB/s |", "|---|---|---|---|---|---|---|"]
+        for fam, key, nbytes, mult, us in cold_rows:
+            g_ = nbytes / (us * 1e-6) / 1e9
+            md.append(f"| {fam} | {key} | {nbytes / 1e6:.1f} | {mult} | {us:.1f} | {g_:.0f} | "
+                      f"{100 * g_ / PEAK_HBM_GBS:.1f} |")
+        md += ["", "| family (weighted) | GB/s | % of 8 TB/s |", "|---|---|---|"]
+        for fam, v in cold.items():
+            if fam != "gemv_by_rows":
+                md.append(f"| {fam} | {v['gbs']:.0f} | {v['pct_hbm_peak']:.1f} |")
+        with open(args.cold_md, "w") as f:
+            f.write("\n".join(md) + "\n")
 
     def gbs(c):
         return c["bytes"] / (c["ms"] * 1e-3) / 1e9 if c["ms"] > 0 else 0.0
@@ -807,6 +995,7 @@ def main():
         "pct_mfma_peak_whole_step": round(100 * lin_flops_step / (ms_per_step * 1e-3) / 1e12
                                           / PEAK_BF16_TFLOPS, 1),
         "adaln_gemv_by_rows": gemv_rows,
+        "cold": cold,
     }
     if args.detail:
         for k, s in sorted(shapes.items()):
@@ -817,7 +1006,7 @@ def main():
                   f"TFLOP/s={s['flops'] / sec / 1e12:8.1f} GB/s={s['bytes'] / sec / 1e9:8.1f} "
                   f"roofline_frac={roof:.3f}", file=sys.stderr)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds, lin_flops_step)
     print(json.dumps(result), flush=True)
 
 
@@ -1076,8 +1265,23 @@ def _oracle_config(cfg, wl):
             "gflops": round(flops / dt / 1e9, 2), "cores": threads}
 
 
-def cpu_baseline(target_s: float):
-    """The CPU oracle (as it stands) on a bounded row sample of the same step's GEMM work."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(target_s: float, step_flops: float = 0.0):
+    """The CPU oracle (as it stands) on a bounded row sample of the same step's GEMM work.
+
+    The oracle splits rows over threads, so its time is linear in the number of rows: the
+    sample's time scaled by M / rows is the full-shape time (labelled "extrapolated")."""
     import numpy as np
 
     import oracle
@@ -1114,15 +1318,24 @@ def cpu_baseline(target_s: float):
     t = time.perf_counter()
     flops = run(rows)
     dt = time.perf_counter() - t
-    return {
-        "value": round(flops / dt / 1e12, 5),
+    rate = flops / dt
+    out = {
+        "value": round(rate / 1e12, 5),
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
         "seconds": round(dt, 2),
         "sample": f"{n} of {M} token rows through rank 0 of tp 4 of the full block (QKV colwise, out-proj "
                   f"rowwise, FFN-up colwise+GELU, FFN-down rowwise); fp64-accumulating C oracle",
+        "cpu_model": _cpu_model(),
+        "nproc": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count(),
+        "cpu_count": os.cpu_count(),
+        "extrapolated_full_shape_s": round(dt * M / n, 2),
+        "extrapolated_note": f"extrapolated (linear in M): the same four GEMMs for all {M} rows of rank 0 of tp 4",
     }
+    if step_flops:
+        out["extrapolated_step_s"] = round(step_flops / rate, 1)
+    return out
 
 
 if __name__ == "__main__":

@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     tp_linear_colwise,
     tp_linear_rowwise,
     tp_linear_rowwise_split_input,
+    tp_linear_tile_rows,
     tp_load_shard,
     tp_load_shard_shape,
     tp_partial_combine,
@@ -27,7 +28,8 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "tp_linear_colwise", "tp_linear_rowwise", "tp_linear_rowwise_split_input", "tp_fused_qkv_split", "tp_partial_combine",
+    "tp_linear_colwise", "tp_linear_rowwise", "tp_linear_rowwise_split_input", "tp_linear_tile_rows",
+    "tp_fused_qkv_split", "tp_partial_combine",
     "tp_plan_shard_slice", "tp_plan_shard_shape", "tp_load_shard", "tp_load_shard_shape", "tp_last_error",
     "load_library", "TPError", "TPValueError", "TPRuntimeError", "TPIOError",
 ]

@@ -172,6 +172,26 @@ tp_status tp_linear_colwise(const void *x, int64_t ldx, const void *w_shard, int
     return run_linear(fn, p, stream);
 }
 
+tp_status tp_linear_tile_rows(int64_t M, int64_t N, int64_t K, tp_act act, int64_t *tile_rows)
+{
+    const char *fn = "tp_linear_tile_rows";
+    g_msg[0] = 0;
+    if (!tile_rows)
+        return fail(TP_ERR_INVALID_ARG, "%s: tile_rows is null", fn);
+    if (act != TP_ACT_NONE && act != TP_ACT_GELU_TANH && act != TP_ACT_SWIGLU)
+        return fail(TP_ERR_INVALID_ARG, "%s: act must be TP_ACT_NONE, TP_ACT_GELU_TANH or TP_ACT_SWIGLU", fn);
+    if (M < 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return fail(TP_ERR_INVALID_ARG, "%s: need 0 <= M, 0 < N, 0 < K, all at most 2^30", fn);
+    tpl::LinearProblem p{};
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.gelu = act == TP_ACT_GELU_TANH;
+    p.swiglu = act == TP_ACT_SWIGLU;
+    *tile_rows = (!p.swiglu && tpl::gemv_supports(M, K)) ? 0 : tpl::gemm_tile_rows(p);
+    return TP_OK;
+}
+
 tp_status tp_linear_rowwise(const void *x_shard, int64_t ldx, const void *w_shard, int64_t ldw,
                             float *partial, int64_t ldp, int64_t M, int64_t N, int64_t k_shard,
                             hipStream_t stream)

@@ -288,6 +288,9 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
     }
     TPL_STEP(read_frags((T - 1) & 1, 1, f1), mma(f0));
     mma(f1);
+    // Keep the epilogue's arithmetic out of the last MFMAs: interleaved with
+    // them, the 256-row GELU and SwiGLU tiles ran out of registers and spilled.
+    __builtin_amdgcn_sched_barrier(0);
 #undef TPL_STEP
 }
 
@@ -324,8 +327,14 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, con
     constexpr int kOutEs = sizeof(OutT);
     constexpr int kRowElems = WNO + 16 / kOutEs;  // one 16-byte pad per row
     OutT *stage = reinterpret_cast<OutT *>(lds) + c.wave * 16 * kRowElems;
-    const int mrow = c.lane & 15;
-    const int ncol = 4 * (c.lane >> 4);
+    // The lane's terms are derived here from an opaque copy of the thread index, so the
+    // compiler cannot keep them live through the main loop (at 256 registers the 256-row
+    // tiles would spill them).
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int mrow = lane & 15;
+    const int ncol = 4 * (lane >> 4);
     auto bias4 = [&](int e) {
         const bf16x4 bb = *reinterpret_cast<const bf16x4 *>(p.bias + e);
         return f32x4{(float)bb[0], (float)bb[1], (float)bb[2], (float)bb[3]};
@@ -333,8 +342,9 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, con
     constexpr int kVec = 16 / kOutEs;              // elements per 16-byte vector
     constexpr int kVecPerRow = WNO / kVec;
     constexpr int kRowsPerPass = 64 / kVecPerRow;
-    const int rd_row = c.lane / kVecPerRow;
-    const int rd_vec = c.lane % kVecPerRow;
+    const int rd_row = lane / kVecPerRow;
+    const int rd_vec = lane % kVecPerRow;
+    const int64_t lane_off = (int64_t)rd_row * p.ldy + rd_vec * kVec;
 #pragma unroll
     for (int i = 0; i < Tile<NXB>::XB; ++i) {
 #pragma unroll
@@ -364,17 +374,18 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, con
             else
                 *reinterpret_cast<f32x4 *>(dst) = v;
         }
+        // Row r + rd_row of the slice: the row's base and bound are wave-uniform, the lane's
+        // offset is fixed, so no per-row lane value stays live across the unrolled passes.
         const int mbase = m0 + c.wave_m * Tile<NXB>::WM + i * 16;
-        const int ncol0 = n0 + c.wave_n * WNO + rd_vec * kVec;
+        const bool col_ok = n0 + c.wave_n * WNO + rd_vec * kVec < p.N;
+        OutT *ybase = reinterpret_cast<OutT *>(p.y) + n0 + c.wave_n * WNO;
 #pragma unroll
         for (int r = 0; r < 16; r += kRowsPerPass) {
-            const int row = r + rd_row;
-            const int m = mbase + row;
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(stage + row * kRowElems + rd_vec * kVec);
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(stage + (r + rd_row) * kRowElems + rd_vec * kVec);
             // Non-temporal stores: about 1% faster than ordinary ones over a DiT block's
             // GEMMs, with the same fetched and written bytes.
-            if (m < p.M && ncol0 < p.N)
-                __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(reinterpret_cast<OutT *>(p.y) + (int64_t)m * p.ldy + ncol0));
+            if (rd_row < p.M - (mbase + r) && col_ok)
+                __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(ybase + (int64_t)(mbase + r) * p.ldy + lane_off));
         }
     }
 }
@@ -472,6 +483,13 @@ int pick_nxb(int M, int tiles_n, int K, int cus)
 }
 
 }  // namespace
+
+int gemm_tile_rows(const LinearProblem &pr)
+{
+    const int tile_cols = pr.swiglu ? BN / 2 : BN;
+    const int tiles_n = (int)((pr.N + tile_cols - 1) / tile_cols);
+    return 32 * pick_nxb((int)pr.M, tiles_n, (int)pr.K, cu_count());
+}
 
 hipError_t launch_gemm(const LinearProblem &pr, hipStream_t stream)
 {

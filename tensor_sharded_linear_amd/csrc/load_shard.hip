@@ -27,6 +27,8 @@
 #include <unistd.h>
 
 #include <algorithm>
+#include <exception>
+#include <new>
 #include <string>
 #include <thread>
 #include <utility>
@@ -73,7 +75,11 @@ class JsonReader {
 
   private:
     static constexpr int kMaxDepth = 32;
+    // A safetensors header holds a few values per tensor; a cap on the values parsed
+    // bounds the tree a malformed header can make the loader build in host memory.
+    static constexpr int64_t kMaxValues = (int64_t)1 << 20;
     const char *p_, *e_;
+    int64_t values_ = 0;
 
     void ws()
     {
@@ -90,7 +96,7 @@ class JsonReader {
     }
     bool value(Json &v, int depth)
     {
-        if (depth > kMaxDepth || p_ >= e_)
+        if (depth > kMaxDepth || p_ >= e_ || ++values_ > kMaxValues)
             return false;
         switch (*p_) {
         case '{': return object(v, depth);
@@ -615,14 +621,11 @@ struct Fd {
     }
 };
 
-}  // namespace
-
-extern "C" tp_status tp_load_shard(const char *path, const char *name, tp_style style, const int64_t *blocks,
-                                   int num_blocks, int tp_degree, int rank, void *dst, int64_t dst_bytes,
-                                   int64_t *shard_rows, int64_t *shard_cols, tp_dtype *dtype, hipStream_t stream)
+tp_status load_shard(const char *path, const char *name, tp_style style, const int64_t *blocks, int num_blocks,
+                     int tp_degree, int rank, void *dst, int64_t dst_bytes, int64_t *shard_rows,
+                     int64_t *shard_cols, tp_dtype *dtype, hipStream_t stream)
 {
     const char *fn = "tp_load_shard";
-    tpl::last_error_buffer()[0] = 0;
     if (!path || !name)
         return fail(TP_ERR_INVALID_ARG, "%s: path and name must be non-null", fn);
     if (style != TP_COLWISE && style != TP_ROWWISE && style != TP_ROWWISE_SPLIT_INPUT)
@@ -736,4 +739,28 @@ extern "C" tp_status tp_load_shard(const char *path, const char *name, tp_style 
         return fail(TP_ERR_UNSUPPORTED, "%s: internal error: byte runs cover %lld of %lld bytes", fn,
                     (long long)pos, (long long)total);
     return stream_runs(fn, path, f.fd, runs, total, static_cast<char *>(dst), stream);
+}
+
+}  // namespace
+
+// The C entry point: no C++ exception may cross it.  The host-side plan (the header's
+// JSON tree, the byte runs of a rowwise shard, the reader threads) can fail to allocate
+// or to start for a malformed header or a very tall tensor; that is an error status.
+extern "C" tp_status tp_load_shard(const char *path, const char *name, tp_style style, const int64_t *blocks,
+                                   int num_blocks, int tp_degree, int rank, void *dst, int64_t dst_bytes,
+                                   int64_t *shard_rows, int64_t *shard_cols, tp_dtype *dtype, hipStream_t stream)
+{
+    const char *fn = "tp_load_shard";
+    tpl::last_error_buffer()[0] = 0;
+    try {
+        return load_shard(path, name, style, blocks, num_blocks, tp_degree, rank, dst, dst_bytes, shard_rows,
+                          shard_cols, dtype, stream);
+    } catch (const std::bad_alloc &) {
+        return fail(TP_ERR_UNSUPPORTED, "%s: out of host memory while planning the read of \"%s\"", fn,
+                    name ? name : "");
+    } catch (const std::exception &e) {
+        return fail(TP_ERR_IO, "%s: %s", fn, e.what());
+    } catch (...) {
+        return fail(TP_ERR_IO, "%s: unexpected exception", fn);
+    }
 }

@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     syms = declared_symbols()
     assert syms == {"tp_linear_colwise", "tp_linear_rowwise", "tp_linear_rowwise_split_input",
                     "tp_fused_qkv_split", "tp_partial_combine", "tp_plan_shard_slice", "tp_load_shard",
-                    "tp_last_error"}
+                    "tp_linear_tile_rows", "tp_last_error"}
     for s in syms:
         assert hasattr(lib, s), s
     assert set(B.SIGNATURES) == syms
@@ -285,3 +285,21 @@ def test_python_binding_rejects_cpu_tensors():
     x = torch.zeros(4, 64, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         tsl.tp_linear_colwise(x, x)
+
+
+def test_tile_rows_query():
+    """The query names the kernel and tile each workload shape runs with.  Without a GPU the
+    library assumes 256 compute units, MI355X's count."""
+    q = tsl.tp_linear_tile_rows
+    assert q(4, 9216, 6144) == 0                   # adaLN rows: weight-streaming kernel
+    assert q(4, 9216, 6144, "swiglu") > 0          # no gated epilogue in the skinny kernel
+    assert q(4608, 2304, 6144) == 192              # 216 tiles, one round
+    assert q(4608, 9216, 6144, "gelu_tanh") == 224  # 756 tiles in three rounds of 256
+    assert q(4608, 6144, 768) == 256               # short k loop: 256-row tiles
+    assert q(4608, 6144, 128, "gelu_tanh") == 256
+    assert q(4608, 3072, 128, "swiglu") == 256     # 128 outputs per SwiGLU tile
+    assert q(0, 16, 64) in (0, 192, 224, 256)
+    with pytest.raises(ValueError):
+        q(-1, 16, 64)
+    with pytest.raises(ValueError):
+        q(16, 16, 64, "relu")

@@ -1,0 +1,60 @@
+"""Device code of libtp_linear.so: no kernel may use per-lane scratch memory.
+
+Every HIP source is compiled for gfx950 to device assembly (no GPU needed), and
+the code-object metadata of every kernel instance is read: a non-zero
+``.private_segment_fixed_size`` means the compiler spilled registers to scratch
+memory, which costs memory traffic in the inner loops and is not allowed for
+any instance the library can launch.
+"""
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "tensor_sharded_linear_amd", "csrc")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+SOURCES = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def kernel_resources(src, tmp_path):
+    """[(kernel symbol, private segment bytes, vgpr count)] for every kernel in src."""
+    from tensor_sharded_linear_amd.build import FLAGS
+    flags = [f for f in FLAGS if f not in ("-shared", "-fPIC")]
+    out = tmp_path / (os.path.basename(src) + ".s")
+    cmd = [HIPCC, *flags, "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           src, "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    text = out.read_text()
+    # the AMDGPU metadata block lists .name, .private_segment_fixed_size, .vgpr_count per kernel
+    kernels = []
+    for block in re.split(r"\n\s+- \.", text.split("amdhsa.kernels:")[1]):
+        name = re.search(r"\.name:\s+(\S+)", block)
+        priv = re.search(r"\.private_segment_fixed_size:\s+(\d+)", block)
+        vgpr = re.search(r"\.vgpr_count:\s+(\d+)", block)
+        if name and priv:
+            kernels.append((name.group(1), int(priv.group(1)), int(vgpr.group(1)) if vgpr else -1))
+    return kernels
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc is not installed")
+@pytest.mark.parametrize("src", SOURCES, ids=[os.path.basename(s) for s in SOURCES])
+def test_no_kernel_spills_to_scratch(src, tmp_path):
+    kernels = kernel_resources(src, tmp_path)
+    text = open(src).read()
+    if "__global__" in text:
+        assert kernels, f"no kernel metadata found for {src}"
+    spilled = [(n, p) for n, p, _ in kernels if p != 0]
+    assert not spilled, f"kernels with scratch (private segment) memory: {spilled}"
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc is not installed")
+def test_every_gemm_instance_is_compiled_and_checked(tmp_path):
+    """The tiled GEMM has 3 tile heights x 2 output types x bias or not x 3 epilogues."""
+    kernels = kernel_resources(os.path.join(CSRC, "gemm_bf16.hip"), tmp_path)
+    gemm = [n for n, _, _ in kernels if "gemm_bf16_nt_kernel" in n]
+    assert len(gemm) == 36, gemm

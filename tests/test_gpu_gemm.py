@@ -21,7 +21,7 @@ import torch
 import oracle
 import synth_inputs as si
 import tensor_sharded_linear_amd as tsl
-from helpers import abs_dot, bits_to_dev, check_close, dev_to_f64
+from helpers import abs_dot, bits_to_dev, check_close, check_swiglu, dev_to_f64, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -305,3 +305,44 @@ def test_skinny_path_reads_only_its_staged_rows(K):
         c = si.normal_bf16(rng, (B, K))
         y = tsl.tp_linear_colwise(bits_to_dev(c), wd, out_dtype=torch.float32)
         check_close(dev_to_f64(y), oracle.colwise(c, w), K, False, S=abs_dot(c, w), what=f"skinny K={K} B={B}")
+
+
+# Two rounds of 256-row tiles (a short k loop keeps 224-row tiles out): the no-bias GELU and
+# SwiGLU epilogues at the largest register footprint of the kernel.  Sampled rows against
+# the oracle include every tile edge; the whole tensor must equal the same call with an
+# all-zero bias (another kernel instance, the same arithmetic per element).
+TALL256 = (4608, 6144, 128)
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_gelu_no_bias_256_row_tiles(out):
+    M, N, K = TALL256
+    assert tsl.tp_linear_tile_rows(M, N, K, "gelu_tanh") == 256
+    rng = np.random.default_rng(41)
+    x = si.normal_bf16(rng, (M, K))
+    w = si.normal_bf16(rng, (N, K), 1 / np.sqrt(K))
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    xd, wd = bits_to_dev(x), bits_to_dev(w)
+    y = tsl.tp_linear_colwise(xd, wd, act="gelu_tanh", out_dtype=dt)
+    rows = sample_rows(M, 32, seed=41, tile=256)
+    ref = oracle.colwise(x, w, None, act=oracle.ACT_GELU_TANH, rows=rows)
+    check_close(dev_to_f64(y[torch.from_numpy(rows).cuda()]), ref, K, out == "bf16",
+                S=abs_dot(x[rows], w), what=f"gelu no bias 256-row tiles {out}")
+    y0 = tsl.tp_linear_colwise(xd, wd, torch.zeros(N, dtype=torch.bfloat16, device="cuda"),
+                               act="gelu_tanh", out_dtype=dt)
+    assert torch.equal(y, y0)
+
+
+def test_swiglu_no_bias_256_row_tiles():
+    M, n, K = 4608, 3072, 128
+    assert tsl.tp_linear_tile_rows(M, n, K, "swiglu") == 256
+    rng = np.random.default_rng(42)
+    x = si.normal_bf16(rng, (M, K))
+    w = si.normal_bf16(rng, (2 * n, K), 1 / np.sqrt(K))
+    xd, wd = bits_to_dev(x), bits_to_dev(w)
+    y = tsl.tp_linear_colwise(xd, wd, act="swiglu")
+    rows = sample_rows(M, 32, seed=42, tile=256)
+    check_swiglu(dev_to_f64(y[torch.from_numpy(rows).cuda()]), x, w, None, True, rows=rows,
+                 what="swiglu no bias 256-row tiles")
+    y0 = tsl.tp_linear_colwise(xd, wd, torch.zeros(2 * n, dtype=torch.bfloat16, device="cuda"), act="swiglu")
+    assert torch.equal(y, y0)

@@ -3,11 +3,14 @@ benchmark times, through the C ABI.
 
 Index work (slices, QKV split, CONCAT) and the SUM combine are checked bit for
 bit on whole tensors.  GEMM outputs are checked against the oracle on sampled
-rows (tile-edge rows plus seeded random rows, all columns, every rank), and on
-whole tensors through GPU-side invariants of the method: the colwise shards'
-outputs gather to the unsharded output, the rowwise partials sum to it (held
-to rounding, not bit for bit: the method does not promise that a sharded and an
-unsharded shape accumulate in the same order).
+rows, all columns, every rank: rows 0, 1 and M - 1, both rows at every edge of
+the output tiles that the library picks for that GEMM's shape (192, 224 or 256
+rows, from tp_linear_tile_rows), and seeded random rows.  Whole tensors are
+checked through GPU-side invariants of the method: the colwise shards' outputs
+gather bit for bit to the unsharded output (the tiled kernel has no split-K, so
+each output element sees the same products in the same order whatever the tile
+height or column offset), and the rowwise partials sum to it (to rounding: the
+sum of P partials and one K-long accumulation add in different orders).
 """
 import numpy as np
 import pytest
@@ -24,6 +27,13 @@ pytestmark = pytest.mark.gpu
 
 def _rows_of(t: torch.Tensor, rows: np.ndarray) -> torch.Tensor:
     return t[torch.from_numpy(rows).to(t.device)]
+
+
+def _edge_rows(m, n, k, act, n_random, seed):
+    """Sample rows at the real tile edges of an [m, k] x [n, k]^T GEMM."""
+    tile = tsl.tp_linear_tile_rows(m, n, k, act)
+    assert tile in (192, 224, 256), tile
+    return sample_rows(m, n_random, seed, tile=tile)
 
 
 def _check_colwise(y, x_bits, w_bits, rows, act, what, bias_bits=None):
@@ -71,7 +81,9 @@ def test_attention_projections_p4():
     wl = si.workload("attention_proj")
     a, m = wl.arrays, wl.meta
     P, H, hd = 4, m["heads"], m["head_dim"]
-    rows = sample_rows(m["M"], 16, seed=1)
+    k_loc = m["hidden"] // P
+    rows_q = _edge_rows(m["M"], 3 * H // P * hd, m["hidden"], "none", 16, seed=1)
+    rows_o = _edge_rows(m["M"], m["hidden"], k_loc, "none", 16, seed=11)
     x, A = bits_to_dev(a["x"]), bits_to_dev(a["a"])
     wqkv, wo = bits_to_dev(a["w_qkv"]), bits_to_dev(a["w_o"])
     qkv_out, parts = [], []
@@ -80,32 +92,31 @@ def test_attention_projections_p4():
         ow, _ = oracle.qkv_split(a["w_qkv"], None, H, hd, P, r)
         assert np.array_equal(dev_to_bits(ws), ow), f"qkv split r{r}"
         y = tsl.tp_linear_colwise(x, ws)
-        _check_colwise(y, a["x"], ow, rows, "none", f"attn qkv r{r}")
+        _check_colwise(y, a["x"], ow, rows_q, "none", f"attn qkv r{r}")
         qkv_out.append(y)
         wos, _ = tsl.tp_plan_shard_slice(wo, None, "rowwise", P, r)
         oo = oracle.shard_rowwise(a["w_o"], P, r)
         assert np.array_equal(dev_to_bits(wos), oo)
-        k_loc = m["hidden"] // P
         p = tsl.tp_linear_rowwise(A[:, r * k_loc:(r + 1) * k_loc], wos)
-        _check_rowwise(_rows_of(p, rows), np.ascontiguousarray(a["a"][rows, r * k_loc:(r + 1) * k_loc]),
+        _check_rowwise(_rows_of(p, rows_o), np.ascontiguousarray(a["a"][rows_o, r * k_loc:(r + 1) * k_loc]),
                        oo, f"attn out-proj r{r}")
         parts.append(p)
     total = tsl.tp_partial_combine(parts, "sum")
     assert np.array_equal(total.cpu().numpy(), oracle.combine_sum([p.cpu().numpy() for p in parts]))
-    check_close(dev_to_f64(_rows_of(total, rows)), oracle.linear(a["a"], a["w_o"], rows=rows), 3072,
-                False, S=abs_dot(a["a"][rows], a["w_o"]), what="attn out-proj sum vs unsharded")
-    # head-aligned shards gather back into the unsharded fused projection (the two runs may
-    # split k differently across workgroups, so they agree to rounding, not bit for bit)
+    check_close(dev_to_f64(_rows_of(total, rows_o)), oracle.linear(a["a"], a["w_o"], rows=rows_o), 3072,
+                False, S=abs_dot(a["a"][rows_o], a["w_o"]), what="attn out-proj sum vs unsharded")
+    # head-aligned shards gather back into the unsharded fused projection, bit for bit
     full = tsl.tp_linear_colwise(x, wqkv)
     cat = tsl.tp_partial_combine(qkv_out, "concat", blocks=[1, 1, 1])
-    check_close(dev_to_f64(cat), dev_to_f64(full), 3072, True, what="attn concat(qkv) vs unsharded")
+    assert torch.equal(cat, full), "attn concat(qkv) differs from the unsharded projection"
 
 
 def test_mlp_p4():
     wl = si.workload("mlp_large")
     a, m = wl.arrays, wl.meta
     P = 4
-    rows = sample_rows(m["M"], 6, seed=2, tile=512)
+    rows_up = _edge_rows(m["M"], m["ffn"] // P, m["hidden"], "gelu_tanh", 6, seed=2)
+    rows_dn = _edge_rows(m["M"], m["hidden"], m["ffn"] // P, "none", 6, seed=12)
     x = bits_to_dev(a["x"])
     w1, w2 = bits_to_dev(a["w1"]), bits_to_dev(a["w2"])
     parts = []
@@ -117,9 +128,9 @@ def test_mlp_p4():
         ow2 = oracle.shard_rowwise(a["w2"], P, r)
         assert np.array_equal(dev_to_bits(w2s), ow2)
         h = tsl.tp_linear_colwise(x, w1s, act="gelu_tanh")
-        _check_colwise(h, a["x"], ow1, rows, "gelu_tanh", f"mlp up r{r}")
+        _check_colwise(h, a["x"], ow1, rows_up, "gelu_tanh", f"mlp up r{r}")
         p = tsl.tp_linear_rowwise(h, w2s)
-        _check_rowwise(_rows_of(p, rows), dev_to_bits(_rows_of(h, rows)), ow2, f"mlp down r{r}")
+        _check_rowwise(_rows_of(p, rows_dn), dev_to_bits(_rows_of(h, rows_dn)), ow2, f"mlp down r{r}")
         parts.append(p)
         del h
     total = tsl.tp_partial_combine(parts, "sum", out_dtype=torch.bfloat16)
@@ -132,7 +143,11 @@ def test_full_block(P):
     wl = si.workload("full_block")
     a, m = wl.arrays, wl.meta
     H, hd, hidden, ffn, M = m["heads"], m["head_dim"], m["hidden"], m["ffn"], m["M"]
-    rows = sample_rows(M, 2, seed=3 + P, tile=1024)
+    kq, k_loc, f_loc = 3 * H // P * hd, hidden // P, ffn // P
+    rows_q = _edge_rows(M, kq, hidden, "none", 2, seed=3 + P)
+    rows_o = _edge_rows(M, hidden, k_loc, "none", 2, seed=13 + P)
+    rows_up = _edge_rows(M, f_loc, hidden, "gelu_tanh", 2, seed=23 + P)
+    rows_dn = _edge_rows(M, hidden, f_loc, "none", 2, seed=33 + P)
     x, A = bits_to_dev(a["x"]), bits_to_dev(a["a"])
     wqkv, wo = bits_to_dev(a["w_qkv"]), bits_to_dev(a["w_o"])
     w1, w2 = bits_to_dev(a["w1"]), bits_to_dev(a["w2"])
@@ -152,15 +167,14 @@ def test_full_block(P):
         assert np.array_equal(dev_to_bits(w2s), o2)
 
         q = tsl.tp_linear_colwise(x, ws)
-        _check_colwise(q, a["x"], oq, rows, "none", f"block P{P} qkv r{r}")
-        k_loc = hidden // P
+        _check_colwise(q, a["x"], oq, rows_q, "none", f"block P{P} qkv r{r}")
         po = tsl.tp_linear_rowwise(A[:, r * k_loc:(r + 1) * k_loc], wos)
-        _check_rowwise(_rows_of(po, rows), np.ascontiguousarray(a["a"][rows, r * k_loc:(r + 1) * k_loc]),
+        _check_rowwise(_rows_of(po, rows_o), np.ascontiguousarray(a["a"][rows_o, r * k_loc:(r + 1) * k_loc]),
                        oo, f"block P{P} out-proj r{r}")
         h = tsl.tp_linear_colwise(x, w1s, act="gelu_tanh")
-        _check_colwise(h, a["x"], o1, rows, "gelu_tanh", f"block P{P} up r{r}")
+        _check_colwise(h, a["x"], o1, rows_up, "gelu_tanh", f"block P{P} up r{r}")
         pd = tsl.tp_linear_rowwise(h, w2s)
-        _check_rowwise(_rows_of(pd, rows), dev_to_bits(_rows_of(h, rows)), o2, f"block P{P} down r{r}")
+        _check_rowwise(_rows_of(pd, rows_dn), dev_to_bits(_rows_of(h, rows_dn)), o2, f"block P{P} down r{r}")
         qkv_out.append(q)
         up_out.append(h)
         out_parts.append(po)
@@ -178,22 +192,22 @@ def test_full_block(P):
     c_up = tsl.tp_partial_combine(up_out, "concat")
     assert np.array_equal(dev_to_bits(c_up), oracle.combine_concat([dev_to_bits(t) for t in up_out]))
 
-    # whole-tensor invariants against the unsharded layers on the GPU (agreement to rounding:
-    # sharded and unsharded runs may split k differently across workgroups)
+    # whole-tensor invariants against the unsharded layers on the GPU: the colwise gathers
+    # bit for bit, the rowwise sum to rounding
     full_qkv = tsl.tp_linear_colwise(x, wqkv)
-    check_close(dev_to_f64(c_qkv), dev_to_f64(full_qkv), hidden, True, what=f"P{P} concat(qkv) vs unsharded")
+    assert torch.equal(c_qkv, full_qkv), f"P{P} concat(qkv) differs from the unsharded projection"
     del full_qkv
     full_up = tsl.tp_linear_colwise(x, w1, act="gelu_tanh")
-    check_close(dev_to_f64(c_up), dev_to_f64(full_up), hidden, True, what=f"P{P} concat(up) vs unsharded")
+    assert torch.equal(c_up, full_up), f"P{P} concat(up) differs from the unsharded projection"
     del full_up
     full_out = tsl.tp_linear_rowwise(A, wo)
     check_close(dev_to_f64(s_out), dev_to_f64(full_out), hidden, False, what=f"P{P} sum(out) vs unsharded")
     del full_out
     # sampled rows of the combined results against the oracle's unsharded layers
-    check_close(dev_to_f64(_rows_of(s_out, rows)), oracle.linear(a["a"], a["w_o"], rows=rows), hidden,
-                False, S=abs_dot(a["a"][rows], a["w_o"]), what=f"P{P} sum(out) vs oracle")
-    hid_rows = dev_to_bits(_rows_of(c_up, rows))
-    check_close(dev_to_f64(_rows_of(s_down, rows)), oracle.linear(hid_rows, a["w2"]), ffn, True,
+    check_close(dev_to_f64(_rows_of(s_out, rows_o)), oracle.linear(a["a"], a["w_o"], rows=rows_o), hidden,
+                False, S=abs_dot(a["a"][rows_o], a["w_o"]), what=f"P{P} sum(out) vs oracle")
+    hid_rows = dev_to_bits(_rows_of(c_up, rows_dn))
+    check_close(dev_to_f64(_rows_of(s_down, rows_dn)), oracle.linear(hid_rows, a["w2"]), ffn, True,
                 S=abs_dot(hid_rows, a["w2"]), what=f"P{P} sum(down) vs oracle")
 
 
