@@ -108,10 +108,11 @@ def check_swiglu(gpu, x_bits, w_bits, b_bits, out_bf16, rows=None, what=""):
     since |silu'| <= 1.1, plus the fp32 evaluation of silu and of the product (a few ulp).
     The stated bar is then applied to the reference mirror-rounded to the output dtype:
     with bf16 output, wherever no bf16 rounding boundary lies within E of the reference,
-    the GPU's value must round to the same bf16 value (|gpu - bf16(ref)| = 0); where one
-    does, either neighbour is correct and the GPU may be one output step away.  rel-L2 is
-    taken against the unrounded reference; every element must also satisfy
-    |gpu - ref| <= E + half an output ulp."""
+    the GPU's value must round to the same bf16 value (|gpu - bf16(ref)| = 0).  Where one
+    does (a reference next to a rounding boundary, or a tiny one whose E spans several
+    output steps), more than one output value is correct, and the element is held to
+    |gpu - ref| <= E + half an output ulp, which every element must satisfy.  rel-L2 is
+    taken against the unrounded reference."""
     import oracle
     n = w_bits.shape[0] // 2
     xs = x_bits if rows is None else x_bits[rows]
@@ -140,8 +141,6 @@ def check_swiglu(gpu, x_bits, w_bits, b_bits, out_bf16, rows=None, what=""):
         wrong = decided & (err_r != 0)
         assert not wrong.any(), (f"{what}: {int(wrong.sum())} outputs rounded differently from the "
                                  f"mirror-rounded reference, worst {float(err_r[wrong].max())}")
-        far = ~decided & (err_r > 2 * hu)
-        assert not far.any(), f"{what}: {int(far.sum())} outputs more than one step from bf16(ref)"
     else:
         max_abs = float(err.max()) if err.size else 0.0
         assert max_abs <= MAX_ABS, f"{what}: max abs error {max_abs} > {MAX_ABS}"
