@@ -810,16 +810,22 @@ def main():
         print(f"probe: {len(launches)} launches per step, {len(g)} of them GEMMs", flush=True)
         return
 
+    import gc
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     T.on = True
+    # No collector pauses on the host while the GPU timeline is timed: a pause long enough to
+    # drain the launch queue would show up inside an event pair.
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gc.enable()
     T.on = False
     ms_per_step = (t1 - t0) * 1e3 / max(args.steps, 1)
     cats, shapes = T.summary()
