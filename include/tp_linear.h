@@ -132,18 +132,20 @@ tp_status tp_linear_rowwise(const void *x_shard, int64_t ldx, const void *w_shar
                             hipStream_t stream);
 
 /*
- * tp_linear_tile_rows -- host-only query of how tp_linear_colwise and
+ * tp_linear_tile_shape -- host-only query of how tp_linear_colwise and
  * tp_linear_rowwise would run a problem of this shape (M rows, N output
  * features, K input features, activation act; for TP_ACT_SWIGLU, N counts the
- * outputs, not the 2 N weight rows) on the current device: *tile_rows receives
- * the rows of the tiled kernel's output tile (256, 224 or 192), or 0 when the
+ * outputs, not the 2 N weight rows) on the current device: *tile_rows and
+ * *tile_cols receive the tiled kernel's output tile (rows 256, 224 or 192;
+ * columns 256 or 192, or 128 outputs with SwiGLU), or both 0 when the
  * weight-streaming kernel would run.  The choice depends on the shape and on
  * the device's compute-unit count.  It lets a caller check results at the
  * tiles' real edges.  No device work, no allocation.
- * Errors: TP_ERR_INVALID_ARG for a null tile_rows, an unknown act, or sizes
- * outside 0 <= M, 0 < N, 0 < K, all at most 2^30.
+ * Errors: TP_ERR_INVALID_ARG for a null output pointer, an unknown act, or
+ * sizes outside 0 <= M, 0 < N, 0 < K, all at most 2^30.
  */
-tp_status tp_linear_tile_rows(int64_t M, int64_t N, int64_t K, tp_act act, int64_t *tile_rows);
+tp_status tp_linear_tile_shape(int64_t M, int64_t N, int64_t K, tp_act act, int64_t *tile_rows,
+                               int64_t *tile_cols);
 
 /*
  * tp_linear_rowwise_split_input -- [TP] "Colwise and rowwise" (the

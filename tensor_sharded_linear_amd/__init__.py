@@ -19,7 +19,7 @@ from ._binding import (  # noqa: F401
     tp_linear_colwise,
     tp_linear_rowwise,
     tp_linear_rowwise_split_input,
-    tp_linear_tile_rows,
+    tp_linear_tile_shape,
     tp_load_shard,
     tp_load_shard_shape,
     tp_partial_combine,
@@ -28,7 +28,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "tp_linear_colwise", "tp_linear_rowwise", "tp_linear_rowwise_split_input", "tp_linear_tile_rows",
+    "tp_linear_colwise", "tp_linear_rowwise", "tp_linear_rowwise_split_input", "tp_linear_tile_shape",
     "tp_fused_qkv_split", "tp_partial_combine",
     "tp_plan_shard_slice", "tp_plan_shard_shape", "tp_load_shard", "tp_load_shard_shape", "tp_last_error",
     "load_library", "TPError", "TPValueError", "TPRuntimeError", "TPIOError",

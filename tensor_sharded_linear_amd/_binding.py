@@ -42,7 +42,7 @@ _I = ctypes.c_int
 SIGNATURES = {
     "tp_linear_colwise": (_I, [_P, _I64, _P, _I64, _P, _P, _I64, _I, _I, _I64, _I64, _I64, _P]),
     "tp_linear_rowwise": (_I, [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _P]),
-    "tp_linear_tile_rows": (_I, [_I64, _I64, _I64, _I, ctypes.POINTER(_I64)]),
+    "tp_linear_tile_shape": (_I, [_I64, _I64, _I64, _I, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "tp_linear_rowwise_split_input": (_I, [_P, _I64, _I64, _P, _I64, _P, _I64, _I64, _I64, _I, _I, _P]),
     "tp_fused_qkv_split": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P]),
     "tp_partial_combine": (_I, [ctypes.POINTER(_P), _I, _I64, _P, _I64, _I, _I, _I, _P,
@@ -192,18 +192,19 @@ def tp_linear_colwise(x: torch.Tensor, w_shard: torch.Tensor, bias: Optional[tor
     return out
 
 
-def tp_linear_tile_rows(m: int, n: int, k: int, act: str = "none") -> int:
-    """Rows of the output tile the tiled kernel uses for an [m, k] x [n, k]^T problem on the
-    current device (256, 224 or 192), or 0 where the weight-streaming kernel runs.  For
-    ``act="swiglu"`` n counts the outputs.  Host-only query: no device work."""
+def tp_linear_tile_shape(m: int, n: int, k: int, act: str = "none") -> tuple:
+    """(rows, cols) of the output tile the tiled kernel uses for an [m, k] x [n, k]^T problem
+    on the current device (rows 256, 224 or 192; cols 256 or 192, 128 with SwiGLU), or (0, 0)
+    where the weight-streaming kernel runs.  For ``act="swiglu"`` n counts the outputs.
+    Host-only query: no device work."""
     lib = load_library()
     try:
         a = {"none": TP_ACT_NONE, "gelu_tanh": TP_ACT_GELU_TANH, "swiglu": TP_ACT_SWIGLU}[act]
     except KeyError:
         raise ValueError("act must be 'none', 'gelu_tanh' or 'swiglu'") from None
-    rows = _I64()
-    _check(lib.tp_linear_tile_rows(m, n, k, a, ctypes.byref(rows)))
-    return rows.value
+    rows, cols = _I64(), _I64()
+    _check(lib.tp_linear_tile_shape(m, n, k, a, ctypes.byref(rows), ctypes.byref(cols)))
+    return rows.value, cols.value
 
 
 def tp_linear_rowwise(x_shard: torch.Tensor, w_shard: torch.Tensor, *,

@@ -172,12 +172,13 @@ tp_status tp_linear_colwise(const void *x, int64_t ldx, const void *w_shard, int
     return run_linear(fn, p, stream);
 }
 
-tp_status tp_linear_tile_rows(int64_t M, int64_t N, int64_t K, tp_act act, int64_t *tile_rows)
+tp_status tp_linear_tile_shape(int64_t M, int64_t N, int64_t K, tp_act act, int64_t *tile_rows,
+                               int64_t *tile_cols)
 {
-    const char *fn = "tp_linear_tile_rows";
+    const char *fn = "tp_linear_tile_shape";
     g_msg[0] = 0;
-    if (!tile_rows)
-        return fail(TP_ERR_INVALID_ARG, "%s: tile_rows is null", fn);
+    if (!tile_rows || !tile_cols)
+        return fail(TP_ERR_INVALID_ARG, "%s: tile_rows and tile_cols must be non-null", fn);
     if (act != TP_ACT_NONE && act != TP_ACT_GELU_TANH && act != TP_ACT_SWIGLU)
         return fail(TP_ERR_INVALID_ARG, "%s: act must be TP_ACT_NONE, TP_ACT_GELU_TANH or TP_ACT_SWIGLU", fn);
     if (M < 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
@@ -188,7 +189,14 @@ tp_status tp_linear_tile_rows(int64_t M, int64_t N, int64_t K, tp_act act, int64
     p.K = K;
     p.gelu = act == TP_ACT_GELU_TANH;
     p.swiglu = act == TP_ACT_SWIGLU;
-    *tile_rows = (!p.swiglu && tpl::gemv_supports(M, K)) ? 0 : tpl::gemm_tile_rows(p);
+    if (!p.swiglu && tpl::gemv_supports(M, K)) {
+        *tile_rows = *tile_cols = 0;
+        return TP_OK;
+    }
+    int rows = 0, cols = 0;
+    tpl::gemm_tile_shape(p, &rows, &cols);
+    *tile_rows = rows;
+    *tile_cols = cols;
     return TP_OK;
 }
 

@@ -9,23 +9,28 @@
 // block of W and X with an fp32 store and no bias (the partial sum).
 //
 // Design for gfx950:
-//  * 256 x 256 output tile per workgroup (224 or 192 rows where that fills
-//    the CUs better), K step 64, 512 threads = 8 waves in a 2 (M) x 4 (N)
-//    grid; each wave owns a 128 x 64 sub-tile held as 8 x 4 MFMA 16x16 fp32
-//    accumulators (128 accumulator registers per lane).  Two
-//    waves per SIMD, so one wave's LDS fragment reads overlap the other's
-//    MFMAs; one wave per SIMD left the LDS read port idle half the time.
-//  * The part runs at its power limit on dense random operands (the same
-//    kernel on all-zero operands is about 35% faster), so energy per flop
-//    sets the speed.  Counting operand reads plus accumulator read and write,
-//    the 16x16x32 form moves 20% fewer register bytes per flop than
-//    32x32x16, and it measured 3-9% faster on every workload shape.
+//  * 256 x 256 output tile per workgroup, or 224 / 192 rows and 192 columns
+//    where that fills the CUs better (pick_tile), K step 64, 512 threads = 8
+//    waves in a 2 (M) x 4 (N) grid; each wave owns a (BM/2) x (BN/4) sub-tile
+//    held as NXB x NWB MFMA 16x16 fp32 accumulators (at most 128 accumulator
+//    registers per lane).  Two waves per SIMD, so one wave's LDS fragment reads
+//    overlap the other's MFMAs.
+//  * On dense random operands the part runs at its power limit.  Counters on
+//    this kernel (MFMA-busy cycles over GUI-active cycles, and GUI-active
+//    cycles over time) show the MFMA pipe busy 64-66% of cycles with random,
+//    constant or all-zero operands alike, while the clock falls from 2.41 GHz
+//    (zeros) to 1.76 GHz (random) back to back; schedule changes that raise
+//    the busy fraction lower the clock by as much.  So energy per flop, and
+//    the fill of the CUs, set the speed.  Counting operand reads plus
+//    accumulator read and write, the 16x16x32 form moves 20% fewer register
+//    bytes per flop than 32x32x16, and it measured 3-9% faster on every
+//    workload shape.
 //  * Operands go HBM/L2 -> LDS by direct-to-LDS DMA (global_load_lds_dwordx4),
-//    no VGPR staging, double-buffered: 2 stages x (X tile + W tile) x 32 KiB =
+//    no VGPR staging, double-buffered: 2 stages x (X tile + W tile), at most
 //    128 KiB of the 160 KiB LDS.
 //  * Fragments are double-buffered in registers at k32 granularity: while
-//    the 32 MFMAs of one k32 step run, the 12 fragments of the next step are
-//    read from LDS, one read after each of the first 12 MFMAs.  The single
+//    the NXB x NWB MFMAs of one k32 step run, the NXB + NWB fragments of the
+//    next step are read from LDS, one read after each of the first MFMAs.  The single
 //    barrier per k-tile sits before the second k32 step: after it the next
 //    k-tile has landed and every wave has finished
 //    reading the stage that the DMA for the k-tile after next then
@@ -39,8 +44,8 @@
 //    operand, so each lane holds runs of four consecutive output columns of
 //    one row.  The epilogue applies bias / GELU / rounding, passes each
 //    16-row slice of a wave's tile through a private LDS area and stores
-//    whole row segments (4 rows x 256 B fp32, 8 rows x 128 B bf16 per
-//    instruction): direct stores from the MFMA layout cover 16 rows x 16 B
+//    whole row segments (with 256-column tiles 4 rows x 256 B fp32 or 8 rows
+//    x 128 B bf16 per instruction): direct stores from the MFMA layout cover 16 rows x 16 B
 //    per instruction and wrote 1.64x the algorithmic bytes for an fp32
 //    output when measured with the 32x32 layout.  The stores are
 //    non-temporal.
@@ -63,23 +68,24 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define TPL_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
-// The tile height is a template parameter NXB, the number of 16-row MFMA
-// blocks per wave: NXB = 8, 7, 6 give 256, 224 and 192 x 256 tiles (the one
-// that fills the CUs best for the shape is chosen, see pick_nxb).
-constexpr int BN = 256;
+// The tile shape is two template parameters, the 16-row MFMA blocks per wave NXB = 8, 7
+// or 6 (256, 224 or 192 rows) and the 16-column blocks per wave NWB = 4 or 3 (256 or
+// 192 columns); pick_tile chooses the one that fills the CUs best for the shape.
 constexpr int BK = 64;
 constexpr int kThreads = 512;     // 8 waves in a 2 (M) x 4 (N) grid
 constexpr int kWavesN = 4;
 constexpr int kWaves = kThreads / 64;
-constexpr int WN = 64;            // columns of the output owned by one wave
-constexpr int WB = WN / 16;       // 16-row W blocks (16-column MFMA tiles) per wave
-constexpr int kDmaW = (BN * BK * 2) / (kThreads * 16);  // 16-byte DMAs per thread per W tile
 
-template <int NXB>
+// NWB = 16-row W blocks (16-column MFMA tiles) per wave: 4 or 3, for 256- or 192-column tiles.
+template <int NXB, int NWB>
 struct Tile {
     static constexpr int XB = NXB;       // 16-row X blocks (16-row MFMA tiles) per wave
+    static constexpr int WB = NWB;
     static constexpr int WM = 16 * NXB;  // rows of the output owned by one wave
+    static constexpr int WN = 16 * NWB;  // columns of the output owned by one wave
     static constexpr int BM = 2 * WM;    // rows of the output tile
+    static constexpr int BN = kWavesN * WN;  // columns of the output tile (weight rows)
+    static constexpr int kDmaW = (BN * BK * 2) / (kThreads * 16);  // 16-byte DMAs per thread per W tile
     static constexpr int kXElems = BM * BK;
     // 16-byte DMAs per thread per X tile.  One DMA instruction of the
     // workgroup moves 64 rows; with an odd NXB the last one covers 32 rows and
@@ -141,11 +147,11 @@ __device__ __forceinline__ float gelu_tanh(float v)
 }
 
 // One k32 step's operand fragments: per lane 8 bf16 of one row of each of
-// the wave's NXB 16-row X blocks and four 16-row W blocks.
-template <int NXB>
+// the wave's NXB 16-row X blocks and NWB 16-row W blocks.
+template <int NXB, int NWB>
 struct Frags {
-    bf16x8 x[Tile<NXB>::XB];
-    bf16x8 w[WB];
+    bf16x8 x[NXB];
+    bf16x8 w[NWB];
 };
 
 // Per-thread constants of the tile pipeline.
@@ -156,7 +162,7 @@ struct Ctx {
     int swz, kh;                  // fragment swizzle and k-quarter
 };
 
-template <int NXB>
+template <int NXB, int NWB>
 __device__ __forceinline__ Ctx make_ctx()
 {
     Ctx c;
@@ -174,8 +180,8 @@ __device__ __forceinline__ Ctx make_ctx()
     // Fragment addressing: lane l reads row (l % 16) of a 16-row block,
     // 16-byte k-chunk (4 s + l / 16) for k32 step s, stored at position
     // chunk ^ ((row >> 1) & 7) = chunk ^ (((l % 16) >> 1) & 7).
-    c.xrow_off = (c.wave_m * Tile<NXB>::WM + (c.lane & 15)) * BK;
-    c.wrow_off = (c.wave_n * WN + (c.lane & 15)) * BK;
+    c.xrow_off = (c.wave_m * Tile<NXB, NWB>::WM + (c.lane & 15)) * BK;
+    c.wrow_off = (c.wave_n * Tile<NXB, NWB>::WN + (c.lane & 15)) * BK;
     c.swz = (c.lane >> 1) & 7;
     c.kh = c.lane >> 4;
     return c;
@@ -196,23 +202,27 @@ __device__ __forceinline__ void dma16(const char *src, uint16_t *dst)
     __builtin_amdgcn_global_load_lds(src, TPL_LDS(dst), 16, 0, 0);
 }
 
-// acc += X[m0 .. m0+BM-1, k] . Wt^T over k-tiles [kt0, kt1), where the 256
-// rows of the W tile Wt are W[n0 .. n0+255] or, GATED, 32-row blocks taken in
+// acc += X[m0 .. m0+BM-1, k] . Wt^T over k-tiles [kt0, kt1), where the BN
+// rows of the W tile Wt are W[n0 .. n0+BN-1] or, GATED (BN = 256), 32-row blocks taken in
 // turn from the gate half W[0 .. N) and the up half W[N .. 2N) of a packed
 // [gate; up] weight: tile row 64 q + 32 h + i is W[h N + n0 + 32 q + i], so
 // wave q's 16-column MFMA blocks 0, 1 hold the gate and blocks 2, 3 the up
 // projection of the same 32 output columns n0 + 32 q + [0, 32).  Rows past the end are clamped
 // (computed and discarded).  Starts with a barrier, so the LDS may still be in
 // use by the caller's previous tile when it is called.
-template <int NXB, bool GATED>
+template <int NXB, int NWB, bool GATED>
 __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, const Ctx &c, int m0, int n0,
-                                         int kt0, int kt1, f32x4 (&acc)[Tile<NXB>::XB][WB])
+                                         int kt0, int kt1, f32x4 (&acc)[NXB][NWB])
 {
     // Per-lane byte offsets (32-bit: operands are below 2 GiB) from
     // wave-uniform bases, so the DMA uses the scalar-base addressing form.
     const char *xbase = reinterpret_cast<const char *>(p.x) + (int64_t)kt0 * BK * 2;
     const char *wbase = reinterpret_cast<const char *>(p.w) + (int64_t)kt0 * BK * 2;
-    typedef Tile<NXB> L;
+    typedef Tile<NXB, NWB> L;
+    static_assert(!GATED || NWB == 4, "the gated tile pairs two gate and two up blocks per wave");
+    constexpr int WB = NWB, kDmaW = L::kDmaW;
+    static_assert(kDmaW * kWaves * 512 == L::BN * BK, "the W DMAs cover the W tile exactly");
+    static_assert(L::kDmaX * kWaves * 512 >= L::kXElems, "the X DMAs cover the X tile");
     uint32_t xoff[L::kDmaX], woff[kDmaW];
 #pragma unroll
     for (int j = 0; j < L::kDmaX; ++j) {
@@ -239,7 +249,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
         for (int j = 0; j < kDmaW; ++j)
             dma16(wb + woff[j], ws + (j * kWaves + c.wave) * 512);
     };
-    auto read_frags = [&](int stage, int s, Frags<NXB> &f) {
+    auto read_frags = [&](int stage, int s, Frags<NXB, NWB> &f) {
         const uint16_t *xs = lds + stage * L::kStageElems;
         const uint16_t *ws = xs + L::kXElems;
         const int cpos = ((s * 4 + c.kh) ^ c.swz) * 8;
@@ -250,7 +260,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
         for (int j = 0; j < WB; ++j)
             f.w[j] = *reinterpret_cast<const bf16x8 *>(ws + c.wrow_off + j * 16 * BK + cpos);
     };
-    auto mma = [&](const Frags<NXB> &f) {
+    auto mma = [&](const Frags<NXB, NWB> &f) {
 #pragma unroll
         for (int i = 0; i < L::XB; ++i)
 #pragma unroll
@@ -269,7 +279,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
         __builtin_amdgcn_sched_group_barrier(0x008, L::XB * WB - (L::XB + WB), 0); \
         __builtin_amdgcn_sched_barrier(0); } while (0)
     const int T = kt1 - kt0;
-    Frags<NXB> f0, f1;
+    Frags<NXB, NWB> f0, f1;
     __syncthreads();  // the LDS is free: the previous tile's reads are done
     issue(0, 0);
     wait_dma();
@@ -315,14 +325,15 @@ constexpr int kActSwiglu = 2;  // W tile = interleaved [gate; up] 32-row blocks,
 // output columns, or 32 with SwiGLU: there its blocks j = 0, 1 hold the gate
 // and j = 2, 3 the up projection of the same 32 columns, and the output is
 // silu(gate + b_gate) * (up + b_up), the bias being [b_gate; b_up] (2 N).
-template <int NXB, bool OUT_BF16, bool HAS_BIAS, int ACT>
+template <int NXB, int NWB, bool OUT_BF16, bool HAS_BIAS, int ACT>
 __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, const Ctx &c, int m0, int n0,
-                                         const f32x4 (&acc)[Tile<NXB>::XB][WB])
+                                         const f32x4 (&acc)[NXB][NWB])
 {
     __syncthreads();  // every wave is done reading the operand stages
     typedef typename std::conditional<OUT_BF16, __bf16, float>::type OutT;
     constexpr bool kGated = ACT == kActSwiglu;
-    constexpr int WNO = kGated ? WN / 2 : WN;  // output columns per wave
+    static_assert(!kGated || NWB == 4, "the gated epilogue pairs two gate and two up blocks");
+    constexpr int WNO = kGated ? Tile<NXB, NWB>::WN / 2 : Tile<NXB, NWB>::WN;  // output columns per wave
     constexpr int JO = WNO / 16;               // 16-column output blocks per wave
     constexpr int kOutEs = sizeof(OutT);
     constexpr int kRowElems = WNO + 16 / kOutEs;  // one 16-byte pad per row
@@ -341,12 +352,16 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, con
     };
     constexpr int kVec = 16 / kOutEs;              // elements per 16-byte vector
     constexpr int kVecPerRow = WNO / kVec;
-    constexpr int kRowsPerPass = 64 / kVecPerRow;
+    // When a pass of 64 lanes covers whole rows, each lane keeps its row and column for
+    // every pass; otherwise (48 output columns per wave) a lane's position moves per pass.
+    constexpr bool kWholeRows = 64 % kVecPerRow == 0;
+    constexpr int kRowsPerPass = kWholeRows ? 64 / kVecPerRow : 1;
+    constexpr int kPasses = (16 * kVecPerRow + 63) / 64;
     const int rd_row = lane / kVecPerRow;
     const int rd_vec = lane % kVecPerRow;
     const int64_t lane_off = (int64_t)rd_row * p.ldy + rd_vec * kVec;
 #pragma unroll
-    for (int i = 0; i < Tile<NXB>::XB; ++i) {
+    for (int i = 0; i < NXB; ++i) {
 #pragma unroll
         for (int j = 0; j < JO; ++j) {
             const int n = n0 + c.wave_n * WNO + j * 16 + ncol;  // N % 16 == 0: n < N covers n + 3
@@ -376,66 +391,94 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, con
         }
         // Row r + rd_row of the slice: the row's base and bound are wave-uniform, the lane's
         // offset is fixed, so no per-row lane value stays live across the unrolled passes.
-        const int mbase = m0 + c.wave_m * Tile<NXB>::WM + i * 16;
-        const bool col_ok = n0 + c.wave_n * WNO + rd_vec * kVec < p.N;
+        const int mbase = m0 + c.wave_m * Tile<NXB, NWB>::WM + i * 16;
         OutT *ybase = reinterpret_cast<OutT *>(p.y) + n0 + c.wave_n * WNO;
+        if constexpr (kWholeRows) {
+            const bool col_ok = n0 + c.wave_n * WNO + rd_vec * kVec < p.N;
 #pragma unroll
-        for (int r = 0; r < 16; r += kRowsPerPass) {
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(stage + (r + rd_row) * kRowElems + rd_vec * kVec);
-            // Non-temporal stores: about 1% faster than ordinary ones over a DiT block's
-            // GEMMs, with the same fetched and written bytes.
-            if (rd_row < p.M - (mbase + r) && col_ok)
-                __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(ybase + (int64_t)(mbase + r) * p.ldy + lane_off));
+            for (int r = 0; r < 16; r += kRowsPerPass) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(stage + (r + rd_row) * kRowElems + rd_vec * kVec);
+                // Non-temporal stores: about 1% faster than ordinary ones over a DiT block's
+                // GEMMs, with the same fetched and written bytes.
+                if (rd_row < p.M - (mbase + r) && col_ok)
+                    __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(ybase + (int64_t)(mbase + r) * p.ldy + lane_off));
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < kPasses; ++q) {
+                const int e = lane + 64 * q;        // vector e of the slice: row e / kVecPerRow
+                const int row = e / kVecPerRow;
+                const int vec = e - row * kVecPerRow;
+                if (row < 16) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(stage + row * kRowElems + vec * kVec);
+                    if (row < p.M - mbase && n0 + c.wave_n * WNO + vec * kVec < p.N)
+                        __builtin_nontemporal_store(
+                            v, reinterpret_cast<f32x4 *>(ybase + (int64_t)(mbase + row) * p.ldy + vec * kVec));
+                }
+            }
         }
     }
 }
 
-template <int NXB>
-__device__ __forceinline__ void zero(f32x4 (&acc)[Tile<NXB>::XB][WB])
+template <int NXB, int NWB>
+__device__ __forceinline__ void zero(f32x4 (&acc)[NXB][NWB])
 {
 #pragma unroll
-    for (int i = 0; i < Tile<NXB>::XB; ++i)
+    for (int i = 0; i < NXB; ++i)
 #pragma unroll
-        for (int j = 0; j < WB; ++j)
+        for (int j = 0; j < NWB; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// One BM x 256 output tile per workgroup (BM x 128 output columns with
-// SwiGLU: the tile's 256 weight rows are 128 gate and 128 up rows).
-template <int NXB, bool OUT_BF16, bool HAS_BIAS, int ACT>
+// One BM x BN output tile per workgroup (BM x 128 output columns with
+// SwiGLU, which always takes BN = 256: the tile's 256 weight rows are 128 gate and
+// 128 up rows).
+template <int NXB, int NWB, bool OUT_BF16, bool HAS_BIAS, int ACT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_nt_kernel(GemmParams p)
 {
-    constexpr int BM = Tile<NXB>::BM;
+    typedef Tile<NXB, NWB> L;
     constexpr bool kGated = ACT == kActSwiglu;
-    constexpr int kTileCols = kGated ? BN / 2 : BN;
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[Tile<NXB>::kLdsElems];
-    const Ctx c = make_ctx<NXB>();
+    constexpr int kTileCols = kGated ? L::BN / 2 : L::BN;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[L::kLdsElems];
+    const Ctx c = make_ctx<NXB, NWB>();
     int tm, tn;
     tile_of(xcd_contiguous(blockIdx.x, p.tiles_m * p.tiles_n), p, tm, tn);
-    f32x4 acc[Tile<NXB>::XB][WB];
-    zero<NXB>(acc);
-    mainloop<NXB, kGated>(p, lds, c, tm * BM, tn * kTileCols, 0, p.K / BK, acc);
-    epilogue<NXB, OUT_BF16, HAS_BIAS, ACT>(p, lds, c, tm * BM, tn * kTileCols, acc);
+    f32x4 acc[NXB][NWB];
+    zero<NXB, NWB>(acc);
+    mainloop<NXB, NWB, kGated>(p, lds, c, tm * L::BM, tn * kTileCols, 0, p.K / BK, acc);
+    epilogue<NXB, NWB, OUT_BF16, HAS_BIAS, ACT>(p, lds, c, tm * L::BM, tn * kTileCols, acc);
 }
 
-template <int NXB, bool OUT_BF16, bool HAS_BIAS, int ACT>
+template <int NXB, int NWB, bool OUT_BF16, bool HAS_BIAS, int ACT>
 hipError_t launch_tm(GemmParams gp, hipStream_t stream)
 {
-    gp.tiles_m = (gp.M + Tile<NXB>::BM - 1) / Tile<NXB>::BM;
+    typedef Tile<NXB, NWB> L;
+    const int tile_cols = ACT == kActSwiglu ? L::BN / 2 : L::BN;
+    gp.tiles_n = (gp.N + tile_cols - 1) / tile_cols;
+    gp.tiles_m = (gp.M + L::BM - 1) / L::BM;
     gp.group_m = gp.tiles_m < 8 ? gp.tiles_m : 8;
-    hipLaunchKernelGGL((gemm_bf16_nt_kernel<NXB, OUT_BF16, HAS_BIAS, ACT>), dim3(gp.tiles_m * gp.tiles_n),
+    hipLaunchKernelGGL((gemm_bf16_nt_kernel<NXB, NWB, OUT_BF16, HAS_BIAS, ACT>), dim3(gp.tiles_m * gp.tiles_n),
                        dim3(kThreads), 0, stream, gp);
     return hipGetLastError();
 }
 
 template <bool OUT_BF16, bool HAS_BIAS, int ACT>
-hipError_t launch_variant(const GemmParams &gp, int nxb, hipStream_t stream)
+hipError_t launch_variant(const GemmParams &gp, int nxb, int nwb, hipStream_t stream)
 {
+    if constexpr (ACT != kActSwiglu) {
+        if (nwb == 3) {
+            switch (nxb) {
+            case 6: return launch_tm<6, 3, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+            case 7: return launch_tm<7, 3, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+            default: return launch_tm<8, 3, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+            }
+        }
+    }
     switch (nxb) {
-    case 6: return launch_tm<6, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
-    case 7: return launch_tm<7, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
-    default: return launch_tm<8, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+    case 6: return launch_tm<6, 4, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+    case 7: return launch_tm<7, 4, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+    default: return launch_tm<8, 4, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
     }
 }
 
@@ -455,27 +498,40 @@ int cu_count()
     return n;
 }
 
-// Tile height: the one with the least cost = (rounds of tiles over the CUs)
-// x (tile rows) x (fragment-read overhead): a wave reads NXB + 4 fragments
-// per 4 NXB MFMAs, so shorter tiles read more per flop (measured about 5% for
-// 192 rows against 256).  Ties go to the taller tile.  224-row tiles are only
-// considered for K >= 3072: with a short k loop the per-tile start and store
-// outweighed the finer quantization (measured in the bench step, rowwise
-// 4608 x 6144: 4-6% faster at K = 4608 and 9216, 2-5% slower at K = 768-2304).
-int pick_nxb(int M, int tiles_n, int K, int cus)
+// Tile shape: the one with the least cost = (rounds of tiles over the CUs) x (tile area)
+// x (cost per flop of the shape).  The per-flop factors are measured in the bench step,
+// where the part runs at its power limit and every byte moved from L2 to LDS costs clock:
+// against 256 x 256, a 224 x 256 tile costs 2.5% more per flop, 192 x 256 5%, 256 x 192
+// 8%, 224 x 192 12% and 192 x 192 27% (rowwise 4608 x 6144 at K = 768-2304: 192 x 192 tiles
+// in three full rounds took 7% longer than 256 x 256 tiles in 1.69 rounds).  224-row tiles
+// are only considered for K >= 3072: with a short k loop the per-tile start and store
+// outweighed the finer quantization.  Ties go to the earlier (larger) shape.  Examples on
+// 256 CUs: 4608 x 2304 x 6144 takes 252 tiles of 224 x 192 (one round) instead of 216 of
+// 192 x 256 (119.8 -> 112.2 us in the bench step), 4608 x 4608 x 6144 504 of them (231.7 ->
+// 225.7 us), 4608 x 9216 x 6144 756 of 224 x 256, rowwise 4608 x 6144 x 2304 432 of 256 x 256.
+struct TileChoice {
+    int nxb, nwb;
+};
+
+TileChoice pick_tile(int M, int N, int K, bool gated, int cus)
 {
-    static const int kNxb[3] = {8, 7, 6};
-    static const double kOverhead[3] = {1.0, 1.025, 1.05};
-    int best = 8;
-    double best_cost = 0;
-    for (int i = 0; i < 3; ++i) {
-        if (kNxb[i] == 7 && K < 3072)
+    struct Cand {
+        int nxb, nwb;
+        double per_flop;
+    };
+    static const Cand kCands[6] = {{8, 4, 1.0}, {7, 4, 1.025}, {6, 4, 1.05},
+                                   {8, 3, 1.08}, {7, 3, 1.12}, {6, 3, 1.27}};
+    TileChoice best{8, 4};
+    double best_cost = -1;
+    for (const Cand &cd : kCands) {
+        if ((gated && cd.nwb != 4) || (cd.nxb == 7 && K < 3072))
             continue;
-        const int bm = 32 * kNxb[i];
-        const int64_t tiles = (int64_t)((M + bm - 1) / bm) * tiles_n;
-        const double cost = (double)((tiles + cus - 1) / cus) * bm * kOverhead[i];
-        if (i == 0 || cost < best_cost) {
-            best = kNxb[i];
+        const int bm = 32 * cd.nxb;
+        const int cols = cd.nwb == 4 ? (gated ? 128 : 256) : 192;
+        const int64_t tiles = (int64_t)((M + bm - 1) / bm) * ((N + cols - 1) / cols);
+        const double cost = (double)((tiles + cus - 1) / cus) * bm * (64 * cd.nwb) * cd.per_flop;
+        if (best_cost < 0 || cost < best_cost) {
+            best = TileChoice{cd.nxb, cd.nwb};
             best_cost = cost;
         }
     }
@@ -484,11 +540,11 @@ int pick_nxb(int M, int tiles_n, int K, int cus)
 
 }  // namespace
 
-int gemm_tile_rows(const LinearProblem &pr)
+void gemm_tile_shape(const LinearProblem &pr, int *rows, int *cols)
 {
-    const int tile_cols = pr.swiglu ? BN / 2 : BN;
-    const int tiles_n = (int)((pr.N + tile_cols - 1) / tile_cols);
-    return 32 * pick_nxb((int)pr.M, tiles_n, (int)pr.K, cu_count());
+    const TileChoice tc = pick_tile((int)pr.M, (int)pr.N, (int)pr.K, pr.swiglu, cu_count());
+    *rows = 32 * tc.nxb;
+    *cols = tc.nwb == 4 ? (pr.swiglu ? 128 : 256) : 192;
 }
 
 hipError_t launch_gemm(const LinearProblem &pr, hipStream_t stream)
@@ -505,24 +561,23 @@ hipError_t launch_gemm(const LinearProblem &pr, hipStream_t stream)
     gp.N = (int)pr.N;
     gp.K = (int)pr.K;
     const int act = pr.swiglu ? kActSwiglu : (pr.gelu ? kActGelu : kActNone);
-    const int tile_cols = pr.swiglu ? BN / 2 : BN;
-    gp.tiles_n = (int)((pr.N + tile_cols - 1) / tile_cols);
-    const int nxb = pick_nxb(gp.M, gp.tiles_n, gp.K, cu_count());
+    const TileChoice tc = pick_tile(gp.M, gp.N, gp.K, pr.swiglu, cu_count());
+    const int nxb = tc.nxb, nwb = tc.nwb;
     const bool bias = pr.bias != nullptr;
     const int sel = (pr.out_bf16 ? 6 : 0) + (bias ? 3 : 0);
     switch (sel + act) {
-    case 0: return launch_variant<false, false, 0>(gp, nxb, stream);
-    case 1: return launch_variant<false, false, 1>(gp, nxb, stream);
-    case 2: return launch_variant<false, false, 2>(gp, nxb, stream);
-    case 3: return launch_variant<false, true, 0>(gp, nxb, stream);
-    case 4: return launch_variant<false, true, 1>(gp, nxb, stream);
-    case 5: return launch_variant<false, true, 2>(gp, nxb, stream);
-    case 6: return launch_variant<true, false, 0>(gp, nxb, stream);
-    case 7: return launch_variant<true, false, 1>(gp, nxb, stream);
-    case 8: return launch_variant<true, false, 2>(gp, nxb, stream);
-    case 9: return launch_variant<true, true, 0>(gp, nxb, stream);
-    case 10: return launch_variant<true, true, 1>(gp, nxb, stream);
-    default: return launch_variant<true, true, 2>(gp, nxb, stream);
+    case 0: return launch_variant<false, false, 0>(gp, nxb, nwb, stream);
+    case 1: return launch_variant<false, false, 1>(gp, nxb, nwb, stream);
+    case 2: return launch_variant<false, false, 2>(gp, nxb, nwb, stream);
+    case 3: return launch_variant<false, true, 0>(gp, nxb, nwb, stream);
+    case 4: return launch_variant<false, true, 1>(gp, nxb, nwb, stream);
+    case 5: return launch_variant<false, true, 2>(gp, nxb, nwb, stream);
+    case 6: return launch_variant<true, false, 0>(gp, nxb, nwb, stream);
+    case 7: return launch_variant<true, false, 1>(gp, nxb, nwb, stream);
+    case 8: return launch_variant<true, false, 2>(gp, nxb, nwb, stream);
+    case 9: return launch_variant<true, true, 0>(gp, nxb, nwb, stream);
+    case 10: return launch_variant<true, true, 1>(gp, nxb, nwb, stream);
+    default: return launch_variant<true, true, 2>(gp, nxb, nwb, stream);
     }
 }
 

@@ -31,8 +31,9 @@ struct LinearProblem {
 
 // Tiled MFMA GEMM (M > kSkinnyMaxM).  Requires K % 64 == 0, N % 16 == 0.
 hipError_t launch_gemm(const LinearProblem &p, hipStream_t stream);
-// Rows of the output tile launch_gemm picks for p on the current device (256, 224 or 192).
-int gemm_tile_rows(const LinearProblem &p);
+// Output tile launch_gemm picks for p on the current device: rows 256, 224 or 192,
+// columns 256 or 192 (128 outputs with SwiGLU).
+void gemm_tile_shape(const LinearProblem &p, int *rows, int *cols);
 
 // Weight-streaming kernel for skinny M (the adaLN modulation shape): each wave
 // holds whole weight rows of up to kSkinnyMaxK elements in registers, and the

@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     syms = declared_symbols()
     assert syms == {"tp_linear_colwise", "tp_linear_rowwise", "tp_linear_rowwise_split_input",
                     "tp_fused_qkv_split", "tp_partial_combine", "tp_plan_shard_slice", "tp_load_shard",
-                    "tp_linear_tile_rows", "tp_last_error"}
+                    "tp_linear_tile_shape", "tp_last_error"}
     for s in syms:
         assert hasattr(lib, s), s
     assert set(B.SIGNATURES) == syms
@@ -287,18 +287,19 @@ def test_python_binding_rejects_cpu_tensors():
         tsl.tp_linear_colwise(x, x)
 
 
-def test_tile_rows_query():
+def test_tile_shape_query():
     """The query names the kernel and tile each workload shape runs with.  Without a GPU the
     library assumes 256 compute units, MI355X's count."""
-    q = tsl.tp_linear_tile_rows
-    assert q(4, 9216, 6144) == 0                   # adaLN rows: weight-streaming kernel
-    assert q(4, 9216, 6144, "swiglu") > 0          # no gated epilogue in the skinny kernel
-    assert q(4608, 2304, 6144) == 192              # 216 tiles, one round
-    assert q(4608, 9216, 6144, "gelu_tanh") == 224  # 756 tiles in three rounds of 256
-    assert q(4608, 6144, 768) == 256               # short k loop: 256-row tiles
-    assert q(4608, 6144, 128, "gelu_tanh") == 256
-    assert q(4608, 3072, 128, "swiglu") == 256     # 128 outputs per SwiGLU tile
-    assert q(0, 16, 64) in (0, 192, 224, 256)
+    q = tsl.tp_linear_tile_shape
+    assert q(4, 9216, 6144) == (0, 0)                     # adaLN rows: weight-streaming kernel
+    assert q(4, 9216, 6144, "swiglu")[0] > 0              # no gated epilogue in the skinny kernel
+    assert q(4608, 2304, 6144) == (224, 192)              # 252 tiles, one round
+    assert q(4608, 4608, 6144, "gelu_tanh") == (224, 192)  # 504 tiles, 1.97 rounds
+    assert q(4608, 9216, 6144, "gelu_tanh") == (224, 256)  # 756 tiles in three rounds of 256
+    assert q(4608, 6144, 768) == (256, 256)               # short k loop: 256-row tiles
+    assert q(4608, 6144, 128, "gelu_tanh") == (256, 256)
+    assert q(4608, 3072, 128, "swiglu") == (256, 128)     # 128 outputs per SwiGLU tile
+    assert q(0, 16, 64)[0] in (0, 192, 224, 256)
     with pytest.raises(ValueError):
         q(-1, 16, 64)
     with pytest.raises(ValueError):

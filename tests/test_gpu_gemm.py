@@ -2,14 +2,14 @@
 weight-streaming kernel) against the oracle, through the C ABI.
 
 Ragged shapes span several tiles with partial tiles on both edges.  The
-kernel picks its tile height per shape (192, 224 or 256 rows, whichever needs
-the least time in rounds of tiles over the CUs; 224 rows only for K >= 3072).
-On a 256-CU device every RAGGED and LARGE shape fits in one round and runs
-192-row tiles.  TALL runs 224-row tiles (504 in two rounds, against 432 of
-256 rows, also two rounds, or 576 of 192 rows in three), so its last tile row
-is ragged inside a tile whose last X DMA instruction is issued by half the
-waves.  WIDE runs 256-row tiles (256 in one round, against 352 of 192 rows in
-two).
+kernel picks its tile shape per problem (192, 224 or 256 rows by 192 or 256
+columns, whichever needs the least time in rounds of tiles over the CUs;
+224 rows only for K >= 3072; tp_linear_tile_shape reports the choice).  On a
+256-CU device the RAGGED shapes and the first LARGE one run 192 x 192 tiles,
+the second LARGE one 224 x 192.  TALL runs 224 x 256 tiles (504 in two
+rounds), so its last tile row is ragged inside a tile whose last X DMA
+instruction is issued by half the waves.  WIDE runs 256 x 256 tiles (256 in
+one round).  test_gpu_tiles.py reaches every tile shape with every epilogue.
 Integer-valued inputs make every summation order exact, so there the GPU must
 equal the oracle bit for bit, which pins operand layout and indexing; random
 inputs are held to the stated tolerance and to the derived per-element bound.
@@ -317,7 +317,7 @@ TALL256 = (4608, 6144, 128)
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 def test_gelu_no_bias_256_row_tiles(out):
     M, N, K = TALL256
-    assert tsl.tp_linear_tile_rows(M, N, K, "gelu_tanh") == 256
+    assert tsl.tp_linear_tile_shape(M, N, K, "gelu_tanh") == (256, 256)
     rng = np.random.default_rng(41)
     x = si.normal_bf16(rng, (M, K))
     w = si.normal_bf16(rng, (N, K), 1 / np.sqrt(K))
@@ -335,7 +335,7 @@ def test_gelu_no_bias_256_row_tiles(out):
 
 def test_swiglu_no_bias_256_row_tiles():
     M, n, K = 4608, 3072, 128
-    assert tsl.tp_linear_tile_rows(M, n, K, "swiglu") == 256
+    assert tsl.tp_linear_tile_shape(M, n, K, "swiglu") == (256, 128)
     rng = np.random.default_rng(42)
     x = si.normal_bf16(rng, (M, K))
     w = si.normal_bf16(rng, (2 * n, K), 1 / np.sqrt(K))
