@@ -7,7 +7,10 @@
 // bound by how fast the weight streams from HBM, so it gets its own kernel:
 //
 //  * one persistent 512-thread workgroup per CU stages the M activation rows
-//    in LDS once (bf16, M * K * 2 bytes);
+//    in LDS once (bf16, M * K * 2 bytes), with every staging load issued
+//    before the first is stored: one memory round trip instead of one per
+//    pass over them (4 rows of 6144 against a cold 9216 x 6144 weight: kernel
+//    21.9 -> 21.1 us, 2 rows 19.6 -> 19.3 us);
 //  * each wave takes whole weight rows n (strided over all waves of the
 //    grid); its 64 lanes read consecutive 16-byte chunks of the row (1 KiB per
 //    instruction, fully coalesced, non-temporal), the whole row in one batch;
@@ -28,6 +31,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
+// Passes of the workgroup over the staged activations: kSkinnyMaxLdsBytes holds at most
+// 96 KiB = 6144 chunks of 16 bytes, 12 per thread.
+constexpr int kStagePasses = (int)(kSkinnyMaxLdsBytes / 16 + kThreads - 1) / kThreads;
 
 struct GemvParams {
     const uint16_t *x;
@@ -134,14 +140,29 @@ __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(GemvParams p, int o
         }                                                                                    \
     } while (0)
 
-    // Issue this wave's first row before staging the activations.
+    // Issue this wave's first row before staging the activations.  The staging loads are
+    // all issued before any of them is stored, so the activations cost one memory round
+    // trip, not one per pass of the workgroup over them.
     if (r0 < p.N)
         TPL_LOAD_ROW(r0, ra);
-    for (int idx = tid; idx < B * nch; idx += kThreads) {
-        const int bb = idx / nch;
-        const int c = idx - bb * nch;
-        *reinterpret_cast<bf16x8 *>(xs + bb * pitch + c * 8) =
-            *reinterpret_cast<const bf16x8 *>(p.x + (int64_t)bb * p.ldx + c * 8);
+    {
+        bf16x8 stg[kStagePasses];
+#pragma unroll
+        for (int i = 0; i < kStagePasses; ++i) {
+            const int idx = tid + i * kThreads;
+            if (idx < B * nch) {
+                const int bb = idx / nch;
+                stg[i] = *reinterpret_cast<const bf16x8 *>(p.x + (int64_t)bb * p.ldx + (idx - bb * nch) * 8);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kStagePasses; ++i) {
+            const int idx = tid + i * kThreads;
+            if (idx < B * nch) {
+                const int bb = idx / nch;
+                *reinterpret_cast<bf16x8 *>(xs + bb * pitch + (idx - bb * nch) * 8) = stg[i];
+            }
+        }
     }
     if (tid < B)
         *reinterpret_cast<bf16x8 *>(xs + tid * pitch + p.K) = bf16x8{};

@@ -13,14 +13,15 @@
 // sweep a row with the widest vector (16, 8, 4 or 2 bytes) that every address,
 // stride and row length of the launch allows.
 //
-// Stores: when every segment's destination is one contiguous range (a shard
-// slice, the QKV split) the kernel stores non-temporally, so the freshly
-// written shard does not sit dirty in the caches that the next kernels (the
-// GEMMs reading it) use: measured 3% faster GEMMs and a 2% shorter step.
-// Strided destinations (CONCAT: column blocks of each output row, whose ends
-// fall inside 128-byte lines) keep ordinary stores, which let the L2 merge the
-// pieces that neighbouring segments write into the same lines (non-temporal
-// stores there measured 13% slower).
+// Stores are ordinary ones.  Strided destinations (CONCAT: column blocks of
+// each output row, whose ends fall inside 128-byte lines) need them so the L2
+// merges the pieces that neighbouring segments write into the same lines
+// (non-temporal stores there measured 13% slower).  Contiguous destinations
+// (shard slices, the QKV split) reach 79-83% of HBM peak cold with ordinary
+// stores against 69-76% with non-temporal ones (kernel durations of single
+// calls after the Infinity Cache is evicted, 226 MB slices); the non-temporal
+// form left the GEMMs after the slices in a bench step 0.5% faster, which does
+// not make up for it.
 #include "tp_internal.h"
 
 namespace tpl {
@@ -56,7 +57,7 @@ __host__ __device__ inline int short_row_block(int n)
     return kThreads >> tz;
 }
 
-template <int VEC, bool NT_STORE>
+template <int VEC>
 __global__ __launch_bounds__(kThreads) void copy_segments_kernel(CopyArgs a)
 {
     typedef typename VecType<VEC>::T V;
@@ -74,11 +75,7 @@ __global__ __launch_bounds__(kThreads) void copy_segments_kernel(CopyArgs a)
                 const int q = f / n;
                 const int v = f - q * n;
                 const V t = __builtin_nontemporal_load(reinterpret_cast<const V *>(s.src + (r0 + q) * s.src_ld) + v);
-                V *dst = reinterpret_cast<V *>(s.dst + (r0 + q) * s.dst_ld) + v;
-                if (NT_STORE)
-                    __builtin_nontemporal_store(t, dst);
-                else
-                    *dst = t;
+                reinterpret_cast<V *>(s.dst + (r0 + q) * s.dst_ld)[v] = t;
             }
         }
         return;
@@ -87,11 +84,7 @@ __global__ __launch_bounds__(kThreads) void copy_segments_kernel(CopyArgs a)
         const V *src = reinterpret_cast<const V *>(s.src + r * s.src_ld);
         V *dst = reinterpret_cast<V *>(s.dst + r * s.dst_ld);
         for (int64_t v = threadIdx.x; v < nv; v += kThreads) {
-            const V t = __builtin_nontemporal_load(src + v);
-            if (NT_STORE)
-                __builtin_nontemporal_store(t, dst + v);
-            else
-                dst[v] = t;
+            dst[v] = __builtin_nontemporal_load(src + v);
         }
     }
 }
@@ -104,11 +97,9 @@ hipError_t launch_copy_segments(const CopySegment *segs, int nseg, hipStream_t s
         const int cnt = nseg - base < kMaxSegmentsPerLaunch ? nseg - base : kMaxSegmentsPerLaunch;
         CopyArgs a;
         uint64_t bits = 0;
-        bool contiguous_dst = true;  // every destination one contiguous range
         for (int i = 0; i < cnt; ++i) {
             const CopySegment &s = segs[base + i];
             a.seg[i] = s;
-            contiguous_dst = contiguous_dst && (s.rows <= 1 || s.dst_ld == s.row_bytes);
             bits |= (uint64_t)(uintptr_t)s.src | (uint64_t)(uintptr_t)s.dst | (uint64_t)s.src_ld |
                     (uint64_t)s.dst_ld | (uint64_t)s.row_bytes;
         }
@@ -133,15 +124,11 @@ hipError_t launch_copy_segments(const CopySegment *segs, int nseg, hipStream_t s
         int64_t gx = max_groups < 4096 ? max_groups : 4096;
         const dim3 grid((unsigned)gx, (unsigned)cnt);
         const dim3 block(kThreads);
-        switch (vec * 2 + (contiguous_dst ? 1 : 0)) {
-        case 33: hipLaunchKernelGGL((copy_segments_kernel<16, true>), grid, block, 0, stream, a); break;
-        case 32: hipLaunchKernelGGL((copy_segments_kernel<16, false>), grid, block, 0, stream, a); break;
-        case 17: hipLaunchKernelGGL((copy_segments_kernel<8, true>), grid, block, 0, stream, a); break;
-        case 16: hipLaunchKernelGGL((copy_segments_kernel<8, false>), grid, block, 0, stream, a); break;
-        case 9: hipLaunchKernelGGL((copy_segments_kernel<4, true>), grid, block, 0, stream, a); break;
-        case 8: hipLaunchKernelGGL((copy_segments_kernel<4, false>), grid, block, 0, stream, a); break;
-        case 5: hipLaunchKernelGGL((copy_segments_kernel<2, true>), grid, block, 0, stream, a); break;
-        default: hipLaunchKernelGGL((copy_segments_kernel<2, false>), grid, block, 0, stream, a); break;
+        switch (vec) {
+        case 16: hipLaunchKernelGGL((copy_segments_kernel<16>), grid, block, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((copy_segments_kernel<8>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((copy_segments_kernel<4>), grid, block, 0, stream, a); break;
+        default: hipLaunchKernelGGL((copy_segments_kernel<2>), grid, block, 0, stream, a); break;
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
