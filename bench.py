@@ -269,6 +269,9 @@ def load_bench(args):
 CAL_ROWS, CAL_COLS = 8192, 8192   # calibration copy: a 128 MiB bf16 weight, copied whole (colwise, P = 1)
 
 
+ATTR_LDS = "SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE"
+ATTR_WAIT = ("SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU "
+             "SQ_ACTIVE_INST_LDS GRBM_GUI_ACTIVE TA_TA_BUSY TD_TD_BUSY")
 KERNEL_OF = {"gemm": "gemm_bf16_nt_kernel", "gemv": "gemv_bf16_kernel", "sum": "combine_sum_kernel",
              "slice": "copy_segments_kernel", "concat": "copy_segments_kernel"}
 N_XCC = 8          # GRBM_GUI_ACTIVE is counted per XCD; the CSV value is their sum
@@ -358,12 +361,13 @@ def reduce_counters(probe_json, dirs):
         e["rows"].append(i)
     md = ["# Hardware counters of one bench step, per kernel family and per GEMM shape", "",
           "Commands (run from the repository root on one MI355X; one counter set per run):", "", "```"]
-    for c in ("FETCH_SIZE", "WRITE_SIZE", "MfmaUtil MfmaFlopsBF16 GRBM_GUI_ACTIVE"):
+    for c in ("FETCH_SIZE", "WRITE_SIZE", "MfmaUtil MfmaFlopsBF16 GRBM_GUI_ACTIVE", ATTR_LDS, ATTR_WAIT):
         tag = c.split()[0].lower()
         md.append(f"rocprofv3 --pmc {c} --kernel-trace --output-format csv -d gpurun_out/pmc_{tag} -o run -- "
                   f"python3 bench.py --probe gpurun_out/probe_{tag}.json")
     md += ["python3 bench.py --counters gpurun_out/probe_fetch_size.json gpurun_out/pmc_fetch_size "
-           "gpurun_out/pmc_write_size gpurun_out/pmc_mfmautil", "```", "",
+           "gpurun_out/pmc_write_size gpurun_out/pmc_mfmautil gpurun_out/pmc_sq_lds_idx_active "
+           "gpurun_out/pmc_sq_wave_cycles", "```", "",
            f"`--probe` runs two bench steps untimed, then one copy of a {CAL_ROWS} x {CAL_COLS} bf16 weight "
            f"({probe['cal_bytes']} bytes read, the same written) whose counters calibrate the byte counts.  "
            f"The tables cover the {n} launches of the second step.  Under counter collection every dispatch "
@@ -422,6 +426,32 @@ def reduce_counters(probe_json, dirs):
             tot["n"] += e["n"]
         md += ["", f"Launch-weighted MfmaUtil over the step's {tot['n']} GEMM launches: "
                    f"{tot['busy'] / tot['n']:.1f}%."]
+    # Attribution counters, where a run collected them: per CU cycle (LDS, TA, TD activity) or
+    # per wave cycle (wait and issue states; SQ_WAVE_CYCLES counts in units of 4 cycles, like
+    # the wait and active counters it divides).
+    per_cu = ["SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "TA_TA_BUSY", "TD_TD_BUSY"]
+    per_wave = ["SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                "SQ_ACTIVE_INST_LDS"]
+    have = [c for c in per_cu + per_wave if any(c in p for p in per)]
+    if have:
+        md += ["", "## Where the GEMM's cycles go (attribution counters)", "",
+               "Per CU cycle: the counter summed over the chip / (GUI-active cycles per XCD x 256 CUs).  "
+               "Per wave cycle: the counter / SQ_WAVE_CYCLES (both in units of 4 cycles).", "",
+               "| family: shape | " + " | ".join(c.replace("SQ_", "") for c in have) + " |",
+               "|---|" + "---|" * len(have)]
+        for (cat, key), e in sorted(shp.items()):
+            if cat != "gemm" and cat not in ("sum", "slice", "concat", "gemv"):
+                continue
+            rowsel = e["rows"]
+            vals = []
+            for c in have:
+                num = sum(per[i].get(c, float("nan")) for i in rowsel)
+                if c in per_cu:
+                    den = sum(per[i].get("GRBM_GUI_ACTIVE", float("nan")) for i in rowsel) / N_XCC * 256
+                else:
+                    den = sum(per[i].get("SQ_WAVE_CYCLES", float("nan")) for i in rowsel)
+                vals.append(f"{num / den:.3f}" if den == den and den > 0 else "-")
+            md.append(f"| {cat}: {key} | " + " | ".join(vals) + " |")
     with open(os.path.join(ROOT, "profiles", "dit_block_step_counters.md"), "w") as f:
         f.write("\n".join(md) + "\n")
 

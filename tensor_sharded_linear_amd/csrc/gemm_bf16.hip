@@ -249,23 +249,46 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
         for (int j = 0; j < kDmaW; ++j)
             dma16(wb + woff[j], ws + (j * kWaves + c.wave) * 512);
     };
+    // 256-row tiles run their MFMAs W block by W block, the other heights X block by X
+    // block (each order measured the faster one for its heights in the bench step), and the
+    // fragments are read in the order the MFMAs use them.
+    constexpr bool kLoadsInterleaved = NXB == 8;
     auto read_frags = [&](int stage, int s, Frags<NXB, NWB> &f) {
         const uint16_t *xs = lds + stage * L::kStageElems;
         const uint16_t *ws = xs + L::kXElems;
         const int cpos = ((s * 4 + c.kh) ^ c.swz) * 8;
+        auto rx = [&]() {
 #pragma unroll
-        for (int i = 0; i < L::XB; ++i)
-            f.x[i] = *reinterpret_cast<const bf16x8 *>(xs + c.xrow_off + i * 16 * BK + cpos);
-#pragma unroll
-        for (int j = 0; j < WB; ++j)
-            f.w[j] = *reinterpret_cast<const bf16x8 *>(ws + c.wrow_off + j * 16 * BK + cpos);
-    };
-    auto mma = [&](const Frags<NXB, NWB> &f) {
-#pragma unroll
-        for (int i = 0; i < L::XB; ++i)
+            for (int i = 0; i < L::XB; ++i)
+                f.x[i] = *reinterpret_cast<const bf16x8 *>(xs + c.xrow_off + i * 16 * BK + cpos);
+        };
+        auto rw = [&]() {
 #pragma unroll
             for (int j = 0; j < WB; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.w[j], f.x[i], acc[i][j], 0, 0, 0);
+                f.w[j] = *reinterpret_cast<const bf16x8 *>(ws + c.wrow_off + j * 16 * BK + cpos);
+        };
+        if constexpr (kLoadsInterleaved) {
+            rw();
+            rx();
+        } else {
+            rx();
+            rw();
+        }
+    };
+    auto mma = [&](const Frags<NXB, NWB> &f) {
+        if constexpr (kLoadsInterleaved) {
+#pragma unroll
+            for (int j = 0; j < WB; ++j)
+#pragma unroll
+                for (int i = 0; i < L::XB; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.w[j], f.x[i], acc[i][j], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < L::XB; ++i)
+#pragma unroll
+                for (int j = 0; j < WB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.w[j], f.x[i], acc[i][j], 0, 0, 0);
+        }
     };
     // Pipeline: stage t % 2 holds k-tile t; steps s = 0, 1 are its k32 slices.
     // TPL_STEP(read next, mma current) fixes the order of one step for the
@@ -278,6 +301,19 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
         }                                                                     \
         __builtin_amdgcn_sched_group_barrier(0x008, L::XB * WB - (L::XB + WB), 0); \
         __builtin_amdgcn_sched_barrier(0); } while (0)
+    // Like TPL_STEP, with the loads of a k-tile issued first, one after each of the first
+    // MFMAs, instead of in a burst before them.
+#define TPL_STEP_DMA(DM, RD, MM) do { DM; RD; MM;                              \
+        _Pragma("unroll") for (int g_ = 0; g_ < L::kDmaX + kDmaW; ++g_) {     \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                \
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                \
+        }                                                                     \
+        _Pragma("unroll") for (int g_ = 0; g_ < L::XB + WB; ++g_) {           \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                \
+        }                                                                     \
+        __builtin_amdgcn_sched_group_barrier(0x008, L::XB * WB - (L::XB + WB) - (L::kDmaX + kDmaW), 0); \
+        __builtin_amdgcn_sched_barrier(0); } while (0)
     const int T = kt1 - kt0;
     Frags<NXB, NWB> f0, f1;
     __syncthreads();  // the LDS is free: the previous tile's reads are done
@@ -287,7 +323,20 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
     read_frags(0, 0, f0);
     if (T > 1)
         issue(1, BK);
-    for (int t = 0; t < T - 1; ++t) {
+    int t = 0;
+    if constexpr (kLoadsInterleaved) {
+        // k-tiles whose successor-but-one exists: its loads go out one per MFMA at the start
+        // of the second k32 step, ahead of the fragment reads (256-row tiles: the burst of
+        // loads before the step left the MFMA pipe idle; 2-3% on the short-K rowwise shapes)
+        for (; t < T - 2; ++t) {
+            const int st = t & 1;
+            TPL_STEP(read_frags(st, 1, f1), mma(f0));
+            wait_dma();
+            __syncthreads();
+            TPL_STEP_DMA(issue(st, (t + 2) * BK), read_frags(st ^ 1, 0, f0), mma(f1));
+        }
+    }
+    for (; t < T - 1; ++t) {
         const int st = t & 1;
         TPL_STEP(read_frags(st, 1, f1), mma(f0));
         wait_dma();
@@ -302,6 +351,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
     // them, the 256-row GELU and SwiGLU tiles ran out of registers and spilled.
     __builtin_amdgcn_sched_barrier(0);
 #undef TPL_STEP
+#undef TPL_STEP_DMA
 }
 
 // SiLU (Swish): v * sigmoid(v) = v / (1 + exp(-v)) = v / (1 + 2^(-v log2(e))),
