@@ -81,6 +81,10 @@ def parse():
                          "rows) for rank 0, cold (a 512 MiB read before each call) and warm, median of --steps "
                          "calls, each against its roofline; the oracle timed beside each workload; writes a "
                          "markdown table to OUT_MD and one JSON line to stdout")
+    ap.add_argument("--cold-trace", nargs=2, metavar=("TRACE_CSV", "COLD_MD"),
+                    help="no GPU: from the rocprofv3 kernel trace of a --cold-md run and the table that run "
+                         "wrote, print the table with each call's kernel duration from the trace (median of "
+                         "its cold dispatches) beside the event-timed one")
     ap.add_argument("--configs-trace", metavar="TRACE_CSV",
                     help="no GPU: from the rocprofv3 kernel trace of a --configs run, print per-kernel medians "
                          "of the dispatches right after the cache-flush read (cold) and of the others (warm)")
@@ -614,6 +618,9 @@ def main():
     if args.configs_trace:
         configs_trace(args.configs_trace)
         return
+    if args.cold_trace:
+        cold_trace(*args.cold_trace)
+        return
     if args.configs:
         configs_bench(args)
         return
@@ -959,7 +966,7 @@ def main():
     if args.cold_md:
         md = ["# Cold per-call times of the step's HBM-bound calls", "",
               "Command (run from the repository root on one MI355X):", "", "```",
-              f"python3 bench.py --cold-md {args.cold_md}", "```", "",
+              "python3 bench.py " + " ".join(sys.argv[1:]), "```", "",
               "After the timed steps, each call below runs once per shape (rank 0) right after a 512 MiB read "
               "that evicts the 256 MB Infinity Cache, timed alone by an event pair on its stream; the figure "
               "is the median of 5.  GB/s is algorithmic bytes (read + write of a copy; every part plus the "
@@ -1227,6 +1234,62 @@ def configs_bench(args):
     with open(args.configs, "w") as fh:
         fh.write("\n".join(md) + "\n")
     print(json.dumps(out), flush=True)
+
+
+COLD_REPS = 5     # cold dispatches per call in the cold table (each after its own flush read)
+FAMILY_KERNEL = {"slice": "copy_segments_kernel", "concat": "copy_segments_kernel", "sum": "combine_sum_kernel",
+                 "gemv": "gemv_bf16_kernel"}
+
+
+def cold_trace(trace_csv, cold_md):
+    """The cold table of a --cold-md run with kernel durations from the same run's rocprofv3 trace.
+
+    The cold section is the last part of the run that reads the flush buffer: its dispatches that
+    directly follow torch's reduction kernel are, in order, COLD_REPS per row of the table.  Each
+    row's kernel family is checked against the dispatch names.  Trace durations carry no event
+    overhead (an event pair adds 1-3 us to a short call)."""
+    import csv
+    import statistics
+
+    recs = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    cold, prev = [], ""
+    for r in recs:
+        name = r["Kernel_Name"]
+        if "reduce_kernel" in prev and any(k in name for k in FAMILY_KERNEL.values()):
+            cold.append((name, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+        prev = name
+    lines = open(cold_md).read().rstrip("\n").split("\n")
+    head = lines.index("| family | call | MB | per step | µs | GB/s | % of 8 TB/s |")
+    rows = []
+    for ln in lines[head + 2:]:
+        if not ln.startswith("| "):
+            break
+        rows.append([c.strip() for c in ln.strip("|").split("|")])
+    need = COLD_REPS * len(rows)
+    if len(cold) < need:
+        raise SystemExit(f"{trace_csv}: {len(cold)} cold dispatches, the table needs {need}")
+    cold = cold[-need:]
+    out = lines[:head] + ["| family | call | MB | per step | µs (events) | % of 8 TB/s (events) | µs (trace) | "
+                          "GB/s (trace) | % of 8 TB/s (trace) |", "|---|---|---|---|---|---|---|---|---|"]
+    fam_tot = {}
+    for i, (fam, key, mb, mult, us, _gbs, pct) in enumerate(rows):
+        names = {n for n, _ in cold[i * COLD_REPS:(i + 1) * COLD_REPS]}
+        if any(FAMILY_KERNEL[fam] not in n for n in names):
+            raise SystemExit(f"row {fam} {key}: trace dispatches are {sorted(names)}")
+        t = statistics.median(u for _, u in cold[i * COLD_REPS:(i + 1) * COLD_REPS])
+        g = float(mb) * 1e6 / (t * 1e-6) / 1e9
+        out.append(f"| {fam} | {key} | {mb} | {mult} | {us} | {pct} | {t:.1f} | {g:.0f} | "
+                   f"{100 * g / PEAK_HBM_GBS:.1f} |")
+        if int(mult):
+            e = fam_tot.setdefault(fam, [0.0, 0.0])
+            e[0] += int(mult) * float(mb) * 1e6
+            e[1] += int(mult) * t * 1e-6
+    out += lines[head + 2 + len(rows):]
+    out += ["", "The trace durations, weighted in the same way:", "",
+            "| family (weighted, trace) | GB/s | % of 8 TB/s |", "|---|---|---|"]
+    for fam, (bb, t) in sorted(fam_tot.items()):
+        out.append(f"| {fam} | {bb / t / 1e9:.0f} | {100 * bb / t / 1e9 / PEAK_HBM_GBS:.1f} |")
+    print("\n".join(out))
 
 
 def configs_trace(path):

@@ -1,0 +1,121 @@
+"""Host-side logic of bench.py that needs no GPU: the one-GPU guard and the reductions of
+rocprofv3 output (cold-call trace, counter runs) on small synthetic files."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+COLD_MD = """# Cold per-call times of the step's HBM-bound calls
+
+Command (run from the repository root on one MI355X):
+
+```
+python3 bench.py --cold-md out.md
+```
+
+| family | call | MB | per step | µs | GB/s | % of 8 TB/s |
+|---|---|---|---|---|---|---|
+| slice | qkv P2 | 200.0 | 2 | 40.0 | 5000 | 62.5 |
+| sum | P2 f32 | 300.0 | 1 | 60.0 | 5000 | 62.5 |
+| gemv | adaLN B1 | 100.0 | 0 | 25.0 | 4000 | 50.0 |
+
+| family (weighted) | GB/s | % of 8 TB/s |
+|---|---|---|
+| slice | 5000 | 62.5 |
+| sum | 5000 | 62.5 |
+"""
+
+
+def _trace(path, rows):
+    """rows: (kernel name, duration ns), one after another."""
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        t = 1000
+        for name, ns in rows:
+            w.writerow([name, t, t + ns])
+            t += ns + 500
+
+
+def test_gpus_above_one_exits_with_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_cold_trace_takes_the_dispatches_after_each_flush(tmp_path, capsys):
+    md = tmp_path / "cold.md"
+    md.write_text(COLD_MD)
+    red = "void at::native::reduce_kernel<512, 1>(...)"
+    rows = [("copy_segments_kernel<16>", 9000), (red, 100000), ("copy_segments_kernel<16>", 7000)]
+    for name, us in (("copy_segments_kernel<16>", [31, 30, 29, 35, 30]),
+                     ("combine_sum_kernel<2, false, false>", [50, 51, 49, 52, 50]),
+                     ("gemv_bf16_kernel<12, 1>", [20, 19, 21, 20, 20])):
+        for u in us:
+            rows += [(red, 100000), (name, u * 1000)]
+    rows.append(("gemv_bf16_kernel<12, 1>", 15000))   # a warm call after the section
+    _trace(tmp_path / "trace.csv", rows)
+    bench.cold_trace(str(tmp_path / "trace.csv"), str(md))
+    out = capsys.readouterr().out
+    # medians 30, 50 and 20 us; 200 MB in 30 us = 6667 GB/s
+    assert "| slice | qkv P2 | 200.0 | 2 | 40.0 | 62.5 | 30.0 | 6667 | 83.3 |" in out
+    assert "| sum | P2 f32 | 300.0 | 1 | 60.0 | 62.5 | 50.0 | 6000 | 75.0 |" in out
+    assert "| gemv | adaLN B1 | 100.0 | 0 | 25.0 | 50.0 | 20.0 | 5000 | 62.5 |" in out
+    # weighted over the step (the GEMV row has weight 0): slice only, then sum only
+    assert "| slice | 6667 | 83.3 |" in out and "| sum | 6000 | 75.0 |" in out
+    assert "| gemv | 5000" not in out
+
+
+def test_cold_trace_rejects_a_family_mismatch(tmp_path):
+    md = tmp_path / "cold.md"
+    md.write_text(COLD_MD)
+    red = "reduce_kernel"
+    rows = []
+    for name in ("copy_segments_kernel", "gemv_bf16_kernel", "gemv_bf16_kernel"):   # sum row gets a GEMV
+        for _ in range(bench.COLD_REPS):
+            rows += [(red, 1000), (name, 1000)]
+    _trace(tmp_path / "trace.csv", rows)
+    with pytest.raises(SystemExit, match="sum P2 f32"):
+        bench.cold_trace(str(tmp_path / "trace.csv"), str(md))
+
+
+def test_counters_scale_bytes_by_the_calibration_copy(tmp_path, monkeypatch):
+    """Two launches (a GEMM and a slice) and the calibration copy; FETCH_SIZE reads half of
+    the true bytes on the copy, so every fetch figure is doubled (slice: 512 B counted -> 1024,
+    plus 1024 written, over 2000 algorithmic)."""
+    cal = 1 << 27
+    probe = {"launches": [["gemm", "colwise 8x8x8", 1024.0, 1000.0], ["slice", "w1 P2", 0.0, 2000.0]],
+             "cal_bytes": cal}
+    pj = tmp_path / "probe.json"
+    pj.write_text(json.dumps(probe))
+    names = ["gemm_bf16_nt_kernel<6, true, false, 0>", "copy_segments_kernel<16>", "copy_segments_kernel<16>"]
+    runs = {"fetch": ("FETCH_SIZE", [1.0, 0.5, cal / 2048]), "write": ("WRITE_SIZE", [0.5, 1.0, cal / 1024])}
+    for tag, (counter, kib) in runs.items():
+        d = tmp_path / tag
+        d.mkdir()
+        with open(d / "run_counter_collection.csv", "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writerow([1, "at::native::fill", counter, 7.0])          # not a library kernel
+            for i, (n, v) in enumerate(zip(names, kib)):
+                w.writerow([i + 2, n, counter, v])
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    bench.reduce_counters(str(pj), [str(tmp_path / "fetch"), str(tmp_path / "write")])
+    t = json.load(open(tmp_path / "traffic.json"))
+    assert t["factors"]["FETCH_SIZE"] == pytest.approx(2.0)
+    assert t["factors"]["WRITE_SIZE"] == pytest.approx(1.0)
+    assert t["fetch_bytes_per_launch"] == 2048       # 1 KiB counted, factor 2
+    assert t["write_bytes_per_launch"] == 512
+    assert t["ratio_to_algorithmic"] == pytest.approx(2.56)
+    md = open(tmp_path / "profiles" / "dit_block_step_counters.md").read()
+    assert "| slice: w1 P2 | 1 | 0.0 | 0.0 | 0.0 | 1.024 |" in md
