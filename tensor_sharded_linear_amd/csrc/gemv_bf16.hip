@@ -7,16 +7,18 @@
 // bound by how fast the weight streams from HBM, so it gets its own kernel:
 //
 //  * one persistent 512-thread workgroup per CU stages the M activation rows
-//    in LDS once (bf16, M * K * 2 bytes), with every staging load issued
-//    before the first is stored: one memory round trip instead of one per
-//    pass over them (4 rows of 6144 against a cold 9216 x 6144 weight: kernel
-//    21.9 -> 21.1 us, 2 rows 19.6 -> 19.3 us);
+//    in LDS once (bf16, M * K * 2 bytes); its staging loads are all issued
+//    before the first is stored, and before the wave's first weight row, so
+//    they cost one memory round trip and the row stays in flight meanwhile;
 //  * each wave takes whole weight rows n (strided over all waves of the
 //    grid); its 64 lanes read consecutive 16-byte chunks of the row (1 KiB per
 //    instruction, fully coalesced, non-temporal), the whole row in one batch;
 //  * the loads of the wave's next row are issued before the current row is
 //    reduced, so every wave keeps a row (K * 2 bytes) in flight while it
-//    computes;
+//    computes.  That holds only while no load sits in a conditional block
+//    (below); with the last rows guarded inside the loop the compiler's waits
+//    kept one row in flight, and a cold 9216 x 6144 weight with 4 rows took
+//    21.2 us instead of 19.3 (36864 x 1536: 22.5 instead of 18.7);
 //  * per chunk and activation row, four v_dot2_f32_bf16 accumulate in fp32;
 //    a butterfly over the 64 lanes (DPP inside 16-lane rows, shuffles across
 //    rows) reduces each row's M sums, and lanes 0..M-1 apply bias / GELU-tanh
@@ -31,9 +33,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-// Passes of the workgroup over the staged activations: kSkinnyMaxLdsBytes holds at most
-// 96 KiB = 6144 chunks of 16 bytes, 12 per thread.
-constexpr int kStagePasses = (int)(kSkinnyMaxLdsBytes / 16 + kThreads - 1) / kThreads;
 
 struct GemvParams {
     const uint16_t *x;
@@ -85,34 +84,52 @@ __device__ __forceinline__ float wave_sum(float v)
 // row's last chunk and pair it with their activation row's zero chunk, so
 // neither the loads nor the dot products branch per lane.  The epilogue options (bias,
 // GELU, output dtype) are uniform runtime flags: they act once per row.
+//
+// No global load sits in a conditional block.  The compiler counts outstanding
+// loads per wave statically; a load that may or may not have been issued forces
+// it to assume the smaller count, and a wait for one row then also waits for the
+// next row's loads, which leaves one row in flight instead of two.  So the
+// staging loads clamp their index, every row load (and the row's bias) is for a
+// row that exists, and the last one or two rows of a wave are peeled out of the
+// loop instead of guarded inside it.  The bias is loaded before the row's chunks,
+// so waiting for it does not wait for them.
 template <int NIT, int B>
 __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(GemvParams p, int out_bf16, int gelu)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [B][K + 8], zeros in the last 8
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nch = p.K >> 3;  // 16-byte chunks per row (K % 64 == 0)
     constexpr int UB = B >= 8 ? 1 : 8 / B;  // chunks per LDS batch (8 vectors)
+    constexpr int kStage = (B * NIT * 64 + kThreads - 1) / kThreads;  // staging loads per thread
+    constexpr int kStage1 = kStage < 8 ? kStage : 8;  // of which issued before the first row
 
     const int pitch = p.K + 8;  // LDS row pitch of the activations
     auto wch = [&](int u) { return min(u * 64 + lane, nch - 1) * 8; };
     auto xch = [&](int u) { return u * 64 + lane < nch ? (u * 64 + lane) * 8 : p.K; };
 
     const int stride = gridDim.x * kWaves;
-    int r0 = blockIdx.x * kWaves + wave;
+    const int first = blockIdx.x * kWaves + wave;                      // this wave's first row
+    const int cnt = first < p.N ? (p.N - first + stride - 1) / stride : 0;  // its rows
+    const uint16_t *bias_src = p.bias ? p.bias : p.w;  // a valid address either way
+    const int lane_out = lane < B ? lane : B - 1;      // lanes past B repeat row B-1's store
     bf16x8 ra[NIT], rb[NIT];
+    uint16_t ba = 0, bb = 0;
 
-#define TPL_LOAD_ROW(n, r)                                                                   \
+#define TPL_LOAD_ROW(i, r, bv)                                                               \
     do {                                                                                     \
-        const uint16_t *src_ = p.w + (int64_t)(n) * p.ldw;                                    \
+        const int n_ = min(first + (i) * stride, p.N - 1);                                    \
+        const uint16_t *src_ = p.w + (int64_t)n_ * p.ldw;                                     \
+        bv = bias_src[n_];                                                                   \
         _Pragma("unroll") for (int u = 0; u < NIT; ++u)                                      \
             r[u] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(src_ + wch(u))); \
         __builtin_amdgcn_sched_barrier(0);                                                   \
     } while (0)
 
-#define TPL_FINISH_ROW(n, r)                                                                 \
+#define TPL_FINISH_ROW(i, r, bv)                                                             \
     do {                                                                                     \
+        const int n_ = first + (i) * stride;                                                  \
         float acc_[B];                                                                       \
         _Pragma("unroll") for (int b = 0; b < B; ++b) acc_[b] = 0.f;                         \
         _Pragma("unroll") for (int u0 = 0; u0 < NIT; u0 += UB) {                             \
@@ -128,59 +145,65 @@ __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(GemvParams p, int o
             __builtin_amdgcn_sched_barrier(0);                                               \
         }                                                                                    \
         _Pragma("unroll") for (int b = 0; b < B; ++b) acc_[b] = wave_sum(acc_[b]);           \
-        if (lane < B) {                                                                      \
-            float v_ = acc_[0];                                                              \
-            _Pragma("unroll") for (int b = 1; b < B; ++b) if (b == lane) v_ = acc_[b];       \
-            if (p.bias) v_ += (float)(*reinterpret_cast<const __bf16 *>(p.bias + (n)));       \
-            if (gelu) v_ = gelu_tanh(v_);                                                    \
-            if (out_bf16)                                                                    \
-                *reinterpret_cast<__bf16 *>(reinterpret_cast<uint16_t *>(p.y) + (int64_t)lane * p.ldy + (n)) = (__bf16)v_; \
-            else                                                                             \
-                reinterpret_cast<float *>(p.y)[(int64_t)lane * p.ldy + (n)] = v_;            \
-        }                                                                                    \
+        float v_ = acc_[0];                                                                  \
+        _Pragma("unroll") for (int b = 1; b < B; ++b) if (b == lane_out) v_ = acc_[b];       \
+        if (p.bias) v_ += (float)__builtin_bit_cast(__bf16, bv);                             \
+        if (gelu) v_ = gelu_tanh(v_);                                                        \
+        if (out_bf16)                                                                        \
+            *reinterpret_cast<__bf16 *>(reinterpret_cast<uint16_t *>(p.y) + (int64_t)lane_out * p.ldy + n_) = (__bf16)v_; \
+        else                                                                                 \
+            reinterpret_cast<float *>(p.y)[(int64_t)lane_out * p.ldy + n_] = v_;             \
     } while (0)
 
-    // Issue this wave's first row before staging the activations.  The staging loads are
-    // all issued before any of them is stored, so the activations cost one memory round
-    // trip, not one per pass of the workgroup over them.
-    if (r0 < p.N)
-        TPL_LOAD_ROW(r0, ra);
+    // The staging loads go first: their LDS stores then wait for them alone, while the
+    // first row's loads stay in flight across the barrier.
     {
-        bf16x8 stg[kStagePasses];
-#pragma unroll
-        for (int i = 0; i < kStagePasses; ++i) {
+        const int last = B * nch - 1;
+        auto stage_load = [&](int i) {
+            const int idx = min(tid + i * kThreads, last);
+            const int bb_ = idx / nch;
+            return *reinterpret_cast<const bf16x8 *>(p.x + (int64_t)bb_ * p.ldx + (idx - bb_ * nch) * 8);
+        };
+        auto stage_store = [&](int i, const bf16x8 &v) {
             const int idx = tid + i * kThreads;
-            if (idx < B * nch) {
-                const int bb = idx / nch;
-                stg[i] = *reinterpret_cast<const bf16x8 *>(p.x + (int64_t)bb * p.ldx + (idx - bb * nch) * 8);
+            if (idx <= last) {
+                const int bb_ = idx / nch;
+                *reinterpret_cast<bf16x8 *>(xs + bb_ * pitch + (idx - bb_ * nch) * 8) = v;
             }
-        }
+        };
+        bf16x8 stg[kStage1];
 #pragma unroll
-        for (int i = 0; i < kStagePasses; ++i) {
-            const int idx = tid + i * kThreads;
-            if (idx < B * nch) {
-                const int bb = idx / nch;
-                *reinterpret_cast<bf16x8 *>(xs + bb * pitch + (idx - bb * nch) * 8) = stg[i];
-            }
-        }
+        for (int i = 0; i < kStage1; ++i)
+            stg[i] = stage_load(i);
+        TPL_LOAD_ROW(0, ra, ba);  // a wave without rows loads row N - 1 and returns below
+#pragma unroll
+        for (int i = 0; i < kStage1; ++i)
+            stage_store(i, stg[i]);
+        // Many activation rows: the rest one at a time (these waits include the first row).
+#pragma unroll
+        for (int i = kStage1; i < kStage; ++i)
+            stage_store(i, stage_load(i));
     }
     if (tid < B)
         *reinterpret_cast<bf16x8 *>(xs + tid * pitch + p.K) = bf16x8{};
     __syncthreads();
+    if (cnt == 0)
+        return;
 
-    // Two rows in flight per wave: A is reduced while B loads, and back.
-    while (r0 < p.N) {
-        const int r1 = r0 + stride;
-        if (r1 < p.N)
-            TPL_LOAD_ROW(r1, rb);
-        TPL_FINISH_ROW(r0, ra);
-        if (r1 >= p.N)
-            break;
-        const int r2 = r1 + stride;
-        if (r2 < p.N)
-            TPL_LOAD_ROW(r2, ra);
-        TPL_FINISH_ROW(r1, rb);
-        r0 = r2;
+    // Two rows in flight per wave: one is reduced while the next loads.
+    int i = 0;
+    for (; i + 2 < cnt; i += 2) {
+        TPL_LOAD_ROW(i + 1, rb, bb);
+        TPL_FINISH_ROW(i, ra, ba);
+        TPL_LOAD_ROW(i + 2, ra, ba);
+        TPL_FINISH_ROW(i + 1, rb, bb);
+    }
+    if (i + 2 == cnt) {
+        TPL_LOAD_ROW(i + 1, rb, bb);
+        TPL_FINISH_ROW(i, ra, ba);
+        TPL_FINISH_ROW(i + 1, rb, bb);
+    } else {
+        TPL_FINISH_ROW(i, ra, ba);
     }
 #undef TPL_LOAD_ROW
 #undef TPL_FINISH_ROW
@@ -204,11 +227,23 @@ hipError_t launch_variant(const GemvParams &gp, bool out_bf16, bool gelu, hipStr
     return hipGetLastError();
 }
 
+// Chunk counts with a kernel instance: a row of K elements takes the smallest
+// one >= ceil(K / 512), so the lanes that re-read a row's last chunk make up
+// less than one iteration.
+constexpr int kNits[] = {1, 2, 3, 4, 6, 8, 12, 16};
+
+int chunk_iters(int64_t K)
+{
+    const int nit = (int)((K / 8 + 63) / 64);
+    for (int n : kNits)
+        if (nit <= n)
+            return n;
+    return 0;
+}
+
 // Largest row count whose row buffers + activation batch fit the 256-register
 // budget of two waves per SIMD without spilling, per chunk count.
-constexpr int max_rows(int nit) { return nit <= 8 ? 8 : (nit <= 12 ? 7 : 3); }
-
-int chunk_iters(int64_t K) { return (int)((K / 8 + 63) / 64); }
+constexpr int max_rows(int nit) { return nit <= 8 ? 8 : (nit <= 12 ? 6 : 2); }
 
 template <int NIT, int B>
 hipError_t launch_if_fits(const GemvParams &gp, bool out_bf16, bool gelu, hipStream_t s)
@@ -239,8 +274,7 @@ bool gemv_supports(int64_t M, int64_t K)
 {
     if (M < 1 || M > kSkinnyMaxM || K > kSkinnyMaxK || M * (K + 8) * 2 > kSkinnyMaxLdsBytes)
         return false;
-    const int nit = chunk_iters(K);
-    return M <= max_rows(nit <= 4 ? 4 : nit <= 8 ? 8 : nit <= 12 ? 12 : 16);
+    return M <= max_rows(chunk_iters(K));
 }
 
 hipError_t launch_gemv(const LinearProblem &pr, hipStream_t stream)
@@ -256,14 +290,17 @@ hipError_t launch_gemv(const LinearProblem &pr, hipStream_t stream)
     gp.M = (int)pr.M;
     gp.N = (int)pr.N;
     gp.K = (int)pr.K;
-    const int nit = chunk_iters(gp.K);
-    if (nit <= 4)
-        return launch_rows<4>(gp, pr.out_bf16, pr.gelu, stream);
-    if (nit <= 8)
-        return launch_rows<8>(gp, pr.out_bf16, pr.gelu, stream);
-    if (nit <= 12)
-        return launch_rows<12>(gp, pr.out_bf16, pr.gelu, stream);
-    return launch_rows<16>(gp, pr.out_bf16, pr.gelu, stream);
+    switch (chunk_iters(gp.K)) {
+    case 1: return launch_rows<1>(gp, pr.out_bf16, pr.gelu, stream);
+    case 2: return launch_rows<2>(gp, pr.out_bf16, pr.gelu, stream);
+    case 3: return launch_rows<3>(gp, pr.out_bf16, pr.gelu, stream);
+    case 4: return launch_rows<4>(gp, pr.out_bf16, pr.gelu, stream);
+    case 6: return launch_rows<6>(gp, pr.out_bf16, pr.gelu, stream);
+    case 8: return launch_rows<8>(gp, pr.out_bf16, pr.gelu, stream);
+    case 12: return launch_rows<12>(gp, pr.out_bf16, pr.gelu, stream);
+    case 16: return launch_rows<16>(gp, pr.out_bf16, pr.gelu, stream);
+    default: return hipErrorInvalidValue;  // K > kSkinnyMaxK, excluded by gemv_supports()
+    }
 }
 
 }  // namespace tpl

@@ -293,6 +293,9 @@ def test_tile_shape_query():
     q = tsl.tp_linear_tile_shape
     assert q(4, 9216, 6144) == (0, 0)                     # adaLN rows: weight-streaming kernel
     assert q(4, 9216, 6144, "swiglu")[0] > 0              # no gated epilogue in the skinny kernel
+    assert q(6, 9216, 6144) == (0, 0) and q(7, 9216, 6144)[0] > 0   # skinny row limit at 12 chunks
+    assert q(8, 9216, 4096) == (0, 0)                     # 8 chunks: all 8 rows
+    assert q(2, 9216, 8192) == (0, 0) and q(3, 9216, 8192)[0] > 0   # 16 chunks: 2 rows
     assert q(4608, 2304, 6144) == (224, 192)              # 252 tiles, one round
     assert q(4608, 4608, 6144, "gelu_tanh") == (224, 192)  # 504 tiles, 1.97 rounds
     assert q(4608, 9216, 6144, "gelu_tanh") == (224, 256)  # 756 tiles in three rounds of 256

@@ -307,6 +307,39 @@ def test_skinny_path_reads_only_its_staged_rows(K):
         check_close(dev_to_f64(y), oracle.colwise(c, w), K, False, S=abs_dot(c, w), what=f"skinny K={K} B={B}")
 
 
+@pytest.mark.parametrize("K", [448, 768, 1536, 2560, 3072, 3584, 4096, 6656, 8192])
+def test_skinny_every_chunk_count_exact(K):
+    """One K per chunk-count instance of the skinny kernel (1, 2, 3, 6, 8, 16 chunks per lane,
+    full and partial), every row count the kernel takes at that K, integer inputs with bias:
+    exact.  N = 2 x 2048 + 16 leaves each wave two or three rows (the peeled last rows)."""
+    rng = np.random.default_rng(90 + K)
+    N = 2 * 2048 + 16
+    w = si.int_bf16(rng, (N, K), -2, 2)
+    b = si.int_bf16(rng, (N,), -8, 8)
+    wd, bd = bits_to_dev(w), bits_to_dev(b)
+    for B in range(1, 9):
+        if tsl.tp_linear_tile_shape(B, N, K) != (0, 0):
+            break                                  # past the kernel's row limit at this K
+        c = si.int_bf16(rng, (B, K), -2, 2)
+        y = tsl.tp_linear_colwise(bits_to_dev(c), wd, bd, out_dtype=torch.float32)
+        assert np.array_equal(dev_to_f64(y), oracle.colwise(c, w, b)), (K, B)
+    assert B >= 2
+
+
+@pytest.mark.parametrize("N", [16, 304, 2048, 2064, 3 * 2048 - 16, 5 * 2048 + 1008])
+def test_skinny_rows_per_wave(N):
+    """Rows per wave from one (a grid smaller than the chip) to six, so that every peeled ending
+    of the row loop runs (2048 waves for N >= 2048)."""
+    rng = np.random.default_rng(N)
+    K = 1024
+    w = si.int_bf16(rng, (N, K), -2, 2)
+    b = si.int_bf16(rng, (N,), -8, 8)
+    for B in (1, 4):
+        c = si.int_bf16(rng, (B, K), -2, 2)
+        y = tsl.tp_linear_colwise(bits_to_dev(c), bits_to_dev(w), bits_to_dev(b), out_dtype=torch.float32)
+        assert np.array_equal(dev_to_f64(y), oracle.colwise(c, w, b)), (N, B)
+
+
 # Two rounds of 256-row tiles (a short k loop keeps 224-row tiles out): the no-bias GELU and
 # SwiGLU epilogues at the largest register footprint of the kernel.  Sampled rows against
 # the oracle include every tile edge; the whole tensor must equal the same call with an
