@@ -13,11 +13,13 @@
 // the buffer that follows the header; an optional "__metadata__" entry maps
 // strings to strings), then that byte buffer.  Tensors are row-major.
 //
-// Host code only.  The rank's slice is a list of byte runs of the file, each
-// mapped to a contiguous range of the shard (one run per packed block for a
-// colwise cut, one per row and block for a rowwise cut).  The runs are read
-// with pread into one of two pinned staging buffers while the host-to-device
-// copy of the other buffer runs on the caller's stream.
+// Host code only.  The rank's slice is a sequence of byte runs of the file,
+// each mapped to a contiguous range of the shard (one run per packed block for
+// a colwise cut, one per row and block for a rowwise cut).  The runs are
+// generated in shard order as the staging chunks are filled, never stored all
+// at once, so the host memory of a load does not grow with the tensor's
+// height.  A chunk is read with pread into one of two pinned staging buffers
+// while the host-to-device copy of the other buffer runs on the caller's stream.
 #include <errno.h>
 #include <fcntl.h>
 #include <stdarg.h>
@@ -327,6 +329,7 @@ constexpr int64_t kMaxHeaderBytes = (int64_t)100 << 20;  // the header is JSON t
 constexpr int64_t kStageBytes = (int64_t)32 << 20;       // each of the two pinned staging buffers
 constexpr int kReadThreads = 8;                          // reader threads per staging chunk
 constexpr int64_t kMinBytesPerThread = (int64_t)1 << 20; // below this a chunk is read by fewer threads
+constexpr size_t kMaxChunkPieces = (size_t)1 << 16;      // pieces per staging chunk (tiny rowwise pieces)
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int kMaxBlocks = 16;
 
@@ -426,19 +429,81 @@ struct Run {
     int64_t file_off, len, dst_off;
 };
 
-void push_run(std::vector<Run> &runs, int64_t file_off, int64_t len, int64_t dst_off)
-{
-    if (len <= 0)
-        return;
-    if (!runs.empty()) {
-        Run &b = runs.back();
-        if (b.file_off + b.len == file_off && b.dst_off + b.len == dst_off) {
-            b.len += len;
-            return;
+// The byte runs of one rank's slice, generated in shard order.  Runs that are
+// contiguous both in the file and in the shard are merged (a colwise cut of
+// one block is a single run; a rowwise cut at tp 1 is one run per tensor).
+class ShardRuns {
+public:
+    // colwise (or 1-D): one run per block, rows of row_bytes; rowwise: per row of
+    // in_f elements and block, `piece[i]` elements starting at `src[i]` of the row,
+    // placed at `loc[i]` of the shard row of `cols` elements.
+    ShardRuns(bool rowwise, int64_t data_begin, int64_t es, int64_t row_bytes, int64_t rows, int64_t in_f,
+              int64_t cols, int nb, const int64_t *piece, const int64_t *src, const int64_t *loc)
+        : rowwise_(rowwise), data_begin_(data_begin), es_(es), row_bytes_(row_bytes), rows_(rowwise ? rows : 1),
+          in_f_(in_f), cols_(cols), nb_(nb)
+    {
+        for (int i = 0; i < nb; ++i) {
+            piece_[i] = piece[i];
+            src_[i] = src[i];
+            loc_[i] = loc[i];
         }
     }
-    runs.push_back(Run{file_off, len, dst_off});
-}
+    // The next run, or false at the end.
+    bool next(Run &out)
+    {
+        if (!raw(out))
+            return false;
+        Run more;
+        while (peek(more) && out.file_off + out.len == more.file_off && out.dst_off + out.len == more.dst_off) {
+            out.len += more.len;
+            have_peek_ = false;
+        }
+        return true;
+    }
+
+private:
+    // The next unmerged run (from the look-ahead if there is one).
+    bool raw(Run &out)
+    {
+        if (have_peek_) {
+            out = peeked_;
+            have_peek_ = false;
+            return true;
+        }
+        while (r_ < rows_) {
+            const int i = i_;
+            const int64_t r = r_;
+            if (++i_ == nb_) {
+                i_ = 0;
+                ++r_;
+            }
+            if (piece_[i] <= 0)
+                continue;
+            if (rowwise_)
+                out = Run{data_begin_ + (r * in_f_ + src_[i]) * es_, piece_[i] * es_, (r * cols_ + loc_[i]) * es_};
+            else
+                out = Run{data_begin_ + src_[i] * row_bytes_, piece_[i] * row_bytes_, loc_[i] * row_bytes_};
+            return true;
+        }
+        return false;
+    }
+    bool peek(Run &out)
+    {
+        if (!have_peek_)
+            have_peek_ = raw(peeked_);
+        out = peeked_;
+        return have_peek_;
+    }
+
+    bool rowwise_;
+    int64_t data_begin_, es_, row_bytes_, rows_, in_f_, cols_;
+    int nb_;
+    int64_t piece_[kMaxBlocks], src_[kMaxBlocks], loc_[kMaxBlocks];
+    int64_t r_ = 0;
+    int i_ = 0;
+    Run peeked_{0, 0, 0};
+    bool have_peek_ = false;
+};
 
 // Reads the pieces of one staging chunk (file offset, length, offset in
 // buf; sorted by that offset, tiling [0, bytes)).  Up to kReadThreads threads
@@ -499,12 +564,12 @@ bool fill_chunk(int fd, char *buf, const std::vector<Run> &pieces, int64_t bytes
     return true;
 }
 
-// Copies the runs (contiguous in destination order) into dst through two
-// pinned staging buffers: while the host-to-device copy of one buffer runs on
-// `stream`, the next chunk is read into the other.  Returns when every copy
-// has completed.
-tp_status stream_runs(const char *fn, const char *path, int fd, const std::vector<Run> &runs, int64_t total,
-                      char *dst, hipStream_t stream)
+// Copies the runs (contiguous in destination order, tiling [0, total)) into
+// dst through two pinned staging buffers: while the host-to-device copy of one
+// buffer runs on `stream`, the next chunk is read into the other.  Returns when
+// every copy has completed.
+tp_status stream_runs(const char *fn, const char *path, int fd, ShardRuns &runs, int64_t total, char *dst,
+                      hipStream_t stream)
 {
     const int64_t cap = total < kStageBytes ? total : kStageBytes;
     void *stage[2] = {nullptr, nullptr};
@@ -514,31 +579,45 @@ tp_status stream_runs(const char *fn, const char *path, int fd, const std::vecto
     hipError_t he = hipSuccess;
     const char *what = "";
 
-    // Cut the runs into staging chunks of at most cap bytes: pieces (file
-    // offset, length, offset in the chunk).
-    std::vector<std::vector<Run>> chunks(1);
-    std::vector<int64_t> chunk_bytes(1, 0);
-    for (const Run &run : runs) {
-        int64_t file_off = run.file_off, len = run.len;
-        while (len > 0) {
-            if (chunk_bytes.back() == cap) {
-                chunks.emplace_back();
-                chunk_bytes.push_back(0);
+    // Staging chunks of at most cap bytes and kMaxChunkPieces pieces (file
+    // offset, length, offset in the chunk), cut from the runs as they come.
+    // The runs must tile [0, total) of the shard in order, so the copies never
+    // leave dst: a run that does not continue where the last one ended fails.
+    Run carry{0, 0, 0};     // the rest of a run that did not fit the last chunk
+    int64_t planned = 0;    // shard bytes handed to chunks so far
+    bool bad_plan = false;
+    auto build_chunk = [&](std::vector<Run> &pieces) -> int64_t {
+        pieces.clear();
+        int64_t bytes = 0;
+        while (!bad_plan && bytes < cap && pieces.size() < kMaxChunkPieces) {
+            if (carry.len == 0) {
+                if (!runs.next(carry))
+                    break;
+                if (carry.dst_off != planned || carry.len <= 0 || carry.len > total - planned) {
+                    bad_plan = true;
+                    carry.len = 0;
+                    break;
+                }
+                planned += carry.len;
             }
-            const int64_t take = len < cap - chunk_bytes.back() ? len : cap - chunk_bytes.back();
-            chunks.back().push_back(Run{file_off, take, chunk_bytes.back()});
-            chunk_bytes.back() += take;
-            file_off += take;
-            len -= take;
+            const int64_t take = carry.len < cap - bytes ? carry.len : cap - bytes;
+            pieces.push_back(Run{carry.file_off, take, bytes});
+            bytes += take;
+            carry.file_off += take;
+            carry.dst_off += take;
+            carry.len -= take;
         }
-    }
+        return bytes;
+    };
+    std::vector<Run> chunk[2];
+    int64_t chunk_bytes[2] = {0, 0};
     // A chunk of a few large pieces announces the next chunk's ranges before it
     // is read, so the storage reads ahead across chunks (chunks of many small
     // pieces announce their own pieces from the reader threads instead).
     constexpr size_t kPrefetchMaxPieces = 64;
-    auto prefetch = [&](size_t c) {
-        if (c < chunks.size() && chunks[c].size() <= kPrefetchMaxPieces)
-            for (const Run &p : chunks[c])
+    auto prefetch = [&](const std::vector<Run> &pieces) {
+        if (pieces.size() <= kPrefetchMaxPieces)
+            for (const Run &p : pieces)
                 (void)posix_fadvise(fd, (off_t)p.file_off, (off_t)p.len, POSIX_FADV_WILLNEED);
     };
     // Allocates staging buffer b on first use, else waits for its last copy.
@@ -570,17 +649,19 @@ tp_status stream_runs(const char *fn, const char *path, int fd, const std::vecto
 
     int cur = 0;
     int64_t chunk_dst = 0;  // shard offset of the current chunk's first byte
-    prefetch(0);
-    for (size_t c = 0; c < chunks.size() && chunk_bytes[c] > 0; ++c) {
+    chunk_bytes[0] = build_chunk(chunk[0]);
+    prefetch(chunk[0]);
+    while (chunk_bytes[cur] > 0) {
         if (!prepare(cur))
             break;
-        prefetch(c + 1);
+        chunk_bytes[cur ^ 1] = build_chunk(chunk[cur ^ 1]);  // the next chunk, for its read-ahead
+        prefetch(chunk[cur ^ 1]);
         int64_t bad = 0;
-        if (!fill_chunk(fd, static_cast<char *>(stage[cur]), chunks[c], chunk_bytes[c], &bad)) {
+        if (!fill_chunk(fd, static_cast<char *>(stage[cur]), chunk[cur], chunk_bytes[cur], &bad)) {
             st = fail(TP_ERR_IO, "%s: %s: read at offset %lld failed", fn, path, (long long)bad);
             break;
         }
-        he = hipMemcpyAsync(dst + chunk_dst, stage[cur], (size_t)chunk_bytes[c], hipMemcpyHostToDevice, stream);
+        he = hipMemcpyAsync(dst + chunk_dst, stage[cur], (size_t)chunk_bytes[cur], hipMemcpyHostToDevice, stream);
         if (he == hipSuccess)
             he = hipEventRecord(ev[cur], stream);
         if (he != hipSuccess) {
@@ -588,7 +669,7 @@ tp_status stream_runs(const char *fn, const char *path, int fd, const std::vecto
             break;
         }
         pending[cur] = true;
-        chunk_dst += chunk_bytes[c];
+        chunk_dst += chunk_bytes[cur];
         cur ^= 1;
     }
     // Every enqueued copy must finish before its staging buffer is freed.
@@ -609,6 +690,9 @@ tp_status stream_runs(const char *fn, const char *path, int fd, const std::vecto
         return st;
     if (he != hipSuccess)
         return fail(TP_ERR_HIP, "%s: %s: HIP error %d (%s)", fn, what, (int)he, hipGetErrorString(he));
+    if (bad_plan || chunk_dst != total)
+        return fail(TP_ERR_UNSUPPORTED, "%s: internal error: byte runs cover %lld of the shard's %lld bytes", fn,
+                    (long long)chunk_dst, (long long)total);
     return TP_OK;
 }
 
@@ -703,41 +787,21 @@ tp_status load_shard(const char *path, const char *name, tp_style style, const i
         return fail(TP_ERR_INVALID_ARG, "%s: dst_bytes=%lld is below the shard's %lld bytes", fn,
                     (long long)dst_bytes, (long long)total);
 
-    // Byte runs of the rank's slice, in shard order.
-    std::vector<Run> runs;
-    int64_t loc = 0, off = 0;
-    if (ti.ndim == 1 || style == TP_COLWISE) {
-        const int64_t row_bytes = (ti.ndim == 1 ? 1 : in_f) * es;
-        for (int i = 0; i < nb; ++i) {
-            const int64_t piece = bl[i] * unit / tp_degree;
-            push_run(runs, ti.data_begin + (off + rank * piece) * row_bytes, piece * row_bytes, loc * row_bytes);
-            loc += piece;
-            off += bl[i] * unit;
-        }
-    } else {
-        runs.reserve((size_t)(out_f * nb));
-        for (int64_t r = 0; r < out_f; ++r) {
-            loc = 0;
-            off = 0;
-            for (int i = 0; i < nb; ++i) {
-                const int64_t piece = bl[i] * unit / tp_degree;
-                push_run(runs, ti.data_begin + (r * in_f + off + rank * piece) * es, piece * es,
-                         (r * cols + loc) * es);
-                loc += piece;
-                off += bl[i] * unit;
-            }
-        }
+    // Byte runs of the rank's slice, in shard order: block i of the sharded dim
+    // holds bl[i] * unit entries, of which the rank takes `piece` starting at
+    // rank * piece; in the shard it lands after the previous blocks' pieces.
+    int64_t piece[kMaxBlocks], src[kMaxBlocks], loc[kMaxBlocks];
+    int64_t at = 0, off = 0;
+    for (int i = 0; i < nb; ++i) {
+        piece[i] = bl[i] * unit / tp_degree;
+        src[i] = off + rank * piece[i];
+        loc[i] = at;
+        at += piece[i];
+        off += bl[i] * unit;
     }
-    // The runs must tile [0, total) of the shard in order: the copies never leave dst.
-    int64_t pos = 0;
-    for (const Run &run : runs) {
-        if (run.dst_off != pos || run.len <= 0)
-            return fail(TP_ERR_UNSUPPORTED, "%s: internal error: byte runs do not tile the shard", fn);
-        pos += run.len;
-    }
-    if (pos != total)
-        return fail(TP_ERR_UNSUPPORTED, "%s: internal error: byte runs cover %lld of %lld bytes", fn,
-                    (long long)pos, (long long)total);
+    const bool rowwise = ti.ndim == 2 && style != TP_COLWISE;
+    ShardRuns runs(rowwise, ti.data_begin, es, (ti.ndim == 1 ? 1 : in_f) * es, out_f, in_f, cols, nb, piece, src,
+                   loc);
     return stream_runs(fn, path, f.fd, runs, total, static_cast<char *>(dst), stream);
 }
 

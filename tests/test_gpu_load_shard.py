@@ -119,3 +119,21 @@ def test_full_size_shard_bit_exact(big_ckpt, style, blocks, P, r):
     b = tsl.tp_load_shard(big_ckpt, "ff.b1", "colwise", P, r, blocks=blocks)
     rb, _ = oracle.load_shard(big_ckpt, "ff.b1", "colwise", P, r, blocks=blocks)
     assert _same(b, rb)
+
+
+@pytest.fixture(scope="module")
+def tall_ckpt(tmp_path_factory):
+    """A tall, narrow tensor: its rowwise shard at tp 8 is 150000 pieces of 4 bytes, more
+    than one staging chunk takes, so the load cuts chunks by piece count as well as bytes."""
+    rng = np.random.default_rng(23)
+    path = str(tmp_path_factory.mktemp("ckpt_tall") / "tall.safetensors")
+    save_file({"tall": _bf16(si.random_bits(rng, (150000, 16)))}, path)
+    return path
+
+
+@pytest.mark.parametrize("style,blocks,P,r", [("rowwise", None, 8, 0), ("rowwise", None, 8, 7),
+                                              ("rowwise", [1, 3], 4, 2), ("colwise", None, 3, 1)])
+def test_tall_tensor_many_pieces_bit_exact(tall_ckpt, style, blocks, P, r):
+    got = tsl.tp_load_shard(tall_ckpt, "tall", style, P, r, blocks=blocks)
+    ref, _ = oracle.load_shard(tall_ckpt, "tall", style, P, r, blocks=blocks)
+    assert _same(got, ref)
