@@ -344,7 +344,7 @@ def reduce_counters(probe_json, dirs):
             if c in cal[1]:
                 scale[c] = probe["cal_bytes"] / (cal[1][c] * 1024.0)
                 scale[c + "_cal_kib"] = cal[1][c]
-        runs.append(f"{d}: {', '.join(sorted(step[0][1][1]))}")
+        runs.append(f"{os.path.basename(os.path.normpath(d))}: {', '.join(sorted(step[0][1][1]))}")
 
     def mean(xs):
         return sum(xs) / len(xs) if xs else float("nan")
@@ -367,11 +367,11 @@ def reduce_counters(probe_json, dirs):
           "Commands (run from the repository root on one MI355X; one counter set per run):", "", "```"]
     for c in ("FETCH_SIZE", "WRITE_SIZE", "MfmaUtil MfmaFlopsBF16 GRBM_GUI_ACTIVE", ATTR_LDS, ATTR_WAIT):
         tag = c.split()[0].lower()
-        md.append(f"rocprofv3 --pmc {c} --kernel-trace --output-format csv -d gpurun_out/pmc_{tag} -o run -- "
-                  f"python3 bench.py --probe gpurun_out/probe_{tag}.json")
-    md += ["python3 bench.py --counters gpurun_out/probe_fetch_size.json gpurun_out/pmc_fetch_size "
-           "gpurun_out/pmc_write_size gpurun_out/pmc_mfmautil gpurun_out/pmc_sq_lds_idx_active "
-           "gpurun_out/pmc_sq_wave_cycles", "```", "",
+        md.append(f"rocprofv3 --pmc {c} --kernel-trace --output-format csv -d out/pmc_{tag} -o run -- "
+                  f"python3 bench.py --probe out/probe_{tag}.json")
+    md += ["python3 bench.py --counters out/probe_fetch_size.json out/pmc_fetch_size "
+           "out/pmc_write_size out/pmc_mfmautil out/pmc_sq_lds_idx_active "
+           "out/pmc_sq_wave_cycles", "```", "",
            f"`--probe` runs two bench steps untimed, then one copy of a {CAL_ROWS} x {CAL_COLS} bf16 weight "
            f"({probe['cal_bytes']} bytes read, the same written) whose counters calibrate the byte counts.  "
            f"The tables cover the {n} launches of the second step.  Under counter collection every dispatch "
