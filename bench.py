@@ -85,6 +85,10 @@ def parse():
                     help="no GPU: from the rocprofv3 kernel trace of a --cold-md run and the table that run "
                          "wrote, print the table with each call's kernel duration from the trace (median of "
                          "its cold dispatches) beside the event-timed one")
+    ap.add_argument("--vendor", metavar="OUT_MD",
+                    help="instead of the step: every GEMM shape of the step through this library and through "
+                         "torch.matmul / torch.mm (hipBLASLt), plain products without epilogue, back to back on "
+                         "three rotating operand sets; writes a markdown table to OUT_MD")
     ap.add_argument("--configs-trace", metavar="TRACE_CSV",
                     help="no GPU: from the rocprofv3 kernel trace of a --configs run, print per-kernel medians "
                          "of the dispatches right after the cache-flush read (cold) and of the others (warm)")
@@ -623,6 +627,9 @@ def main():
         return
     if args.configs:
         configs_bench(args)
+        return
+    if args.vendor:
+        vendor_bench(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -1239,6 +1246,90 @@ def configs_bench(args):
 COLD_REPS = 5     # cold dispatches per call in the cold table (each after its own flush read)
 FAMILY_KERNEL = {"slice": "copy_segments_kernel", "concat": "copy_segments_kernel", "sum": "combine_sum_kernel",
                  "gemv": "gemv_bf16_kernel"}
+
+
+VENDOR_SHAPES = [("colwise", 4608, 2304, 6144), ("colwise", 4608, 4608, 6144), ("colwise", 4608, 9216, 6144),
+                 ("rowwise", 4608, 6144, 768), ("rowwise", 4608, 6144, 1536), ("rowwise", 4608, 6144, 2304),
+                 ("rowwise", 4608, 6144, 3072), ("rowwise", 4608, 6144, 4608), ("rowwise", 4608, 6144, 9216)]
+
+
+def vendor_bench(args):
+    """The step's GEMM shapes (no bias or activation) through this library and through the
+    vendor BLAS that torch calls (hipBLASLt): colwise with bf16 output (torch.matmul), rowwise
+    with fp32 output (torch.mm with out_dtype).  Each measurement is 3 warm-up calls, then 20
+    calls back to back on three rotating operand sets under one event pair (dispatch gaps
+    included, as in the step); the two implementations alternate twice per shape and the
+    faster of each pair of measurements is kept."""
+    import torch
+    import tensor_sharded_linear_amd as tsl
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tsl.load_library()
+    reps, warm = 20, 3
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for i in range(warm):
+            fn(i % 3)
+        e0, e1 = TimingEvent(), TimingEvent()
+        e0.record(stream)
+        for i in range(reps):
+            fn(i % 3)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        e0.destroy()
+        e1.destroy()
+        return us
+
+    rows = []
+    for kind, M, N, K in VENDOR_SHAPES:
+        g = torch.Generator(device=dev)
+        g.manual_seed(M * 7 + N * 3 + K)
+        xs = [torch.randn(M, K, device=dev, generator=g).to(torch.bfloat16) for _ in range(3)]
+        ws = [(torch.randn(N, K, device=dev, generator=g) / K ** 0.5).to(torch.bfloat16) for _ in range(3)]
+        if kind == "colwise":
+            ours = lambda i: tsl.tp_linear_colwise(xs[i], ws[i])
+            vend = lambda i: torch.matmul(xs[i], ws[i].t())
+            vend_note = "torch.matmul, bf16 out"
+        else:
+            ours = lambda i: tsl.tp_linear_rowwise(xs[i], ws[i])
+            try:
+                torch.mm(xs[0], ws[0].t(), out_dtype=torch.float32)
+                vend = lambda i: torch.mm(xs[i], ws[i].t(), out_dtype=torch.float32)
+                vend_note = "torch.mm, fp32 out"
+            except (RuntimeError, TypeError):
+                vend = lambda i: torch.matmul(xs[i], ws[i].t())
+                vend_note = "torch.matmul, bf16 out (no fp32-output product available)"
+        t_ours, t_vend = [], []
+        for _ in range(2):
+            t_ours.append(timed(ours))
+            t_vend.append(timed(vend))
+        a, b = min(t_ours), min(t_vend)
+        fl = 2.0 * M * N * K
+        rows.append(dict(kind=kind, shape=f"{M}x{N}x{K}", ours_us=round(a, 1), ours_tflops=round(fl / a / 1e6, 1),
+                         vendor_us=round(b, 1), vendor_tflops=round(fl / b / 1e6, 1), vendor=vend_note,
+                         tile=tsl.tp_linear_tile_shape(M, N, K)))
+        print(f"# {kind} {M}x{N}x{K}: ours {a:.1f} us, vendor {b:.1f} us", file=sys.stderr, flush=True)
+        del xs, ws
+    md = ["# GEMM shapes of the step: this library against the vendor BLAS (hipBLASLt)", "",
+          "Command (run from the repository root on one MI355X):", "", "```",
+          "python3 bench.py " + " ".join(sys.argv[1:]), "```", "",
+          "Plain products without bias or activation, the shapes of the step's GEMMs (M x N x K: tokens x "
+          "output features x input features).  Each figure: 3 warm-up calls, then 20 calls back to back on "
+          "three rotating operand sets (random normal bf16) under one event pair, so dispatch gaps are "
+          "included as in the step; the two implementations alternate twice per shape, and the faster "
+          "measurement of each is kept.  Percent of the 2.5 PFLOP/s bf16 dense peak.", "",
+          "| product | M x N x K | this library (tile) | µs | TFLOP/s | % | vendor | µs | TFLOP/s | % | vendor / library time |",
+          "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        md.append(f"| {r['kind']} | {r['shape']} | {r['tile'][0]}x{r['tile'][1]} | {r['ours_us']} | "
+                  f"{r['ours_tflops']:.0f} | {100 * r['ours_tflops'] / PEAK_BF16_TFLOPS:.1f} | {r['vendor']} | "
+                  f"{r['vendor_us']} | {r['vendor_tflops']:.0f} | {100 * r['vendor_tflops'] / PEAK_BF16_TFLOPS:.1f} | "
+                  f"{r['vendor_us'] / r['ours_us']:.3f} |")
+    with open(args.vendor, "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(json.dumps({"vendor_comparison": rows}), flush=True)
 
 
 def cold_trace(trace_csv, cold_md):
