@@ -94,7 +94,7 @@ __device__ __forceinline__ float wave_sum(float v)
 // loop instead of guarded inside it.  The bias is loaded before the row's chunks,
 // so waiting for it does not wait for them.
 template <int NIT, int B>
-__global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(GemvParams p, int out_bf16, int gelu)
+__global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(GemvParams p, int out_bf16, int gelu, int wave_major)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [B][K + 8], zeros in the last 8
     const int tid = threadIdx.x;
@@ -110,7 +110,12 @@ __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(GemvParams p, int o
     auto xch = [&](int u) { return u * 64 + lane < nch ? (u * 64 + lane) * 8 : p.K; };
 
     const int stride = gridDim.x * kWaves;
-    const int first = blockIdx.x * kWaves + wave;                      // this wave's first row
+    // This wave's first row.  When the rows do not divide evenly over the waves, the waves
+    // that take one row more are spread over all workgroups (wave-major numbering) instead
+    // of filling the first ones: 9216 rows on 2048 waves, 1 or 2 activation rows, 4% faster
+    // cold.  With an even division the workgroup-major order (each workgroup's waves on
+    // neighbouring rows) measured 1-3% faster.
+    const int first = wave_major ? wave * gridDim.x + blockIdx.x : blockIdx.x * kWaves + wave;
     const int cnt = first < p.N ? (p.N - first + stride - 1) / stride : 0;  // its rows
     const uint16_t *bias_src = p.bias ? p.bias : p.w;  // a valid address either way
     const int lane_out = lane < B ? lane : B - 1;      // lanes past B repeat row B-1's store
@@ -223,7 +228,8 @@ hipError_t launch_variant(const GemvParams &gp, bool out_bf16, bool gelu, hipStr
     int blocks = (gp.N + kWaves - 1) / kWaves;
     if (blocks > 256)
         blocks = 256;
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, stream, gp, (int)out_bf16, (int)gelu);
+    const int wave_major = gp.N % (blocks * kWaves) != 0;
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, stream, gp, (int)out_bf16, (int)gelu, wave_major);
     return hipGetLastError();
 }
 
