@@ -326,6 +326,23 @@ def test_skinny_every_chunk_count_exact(K):
     assert B >= 2
 
 
+@pytest.mark.parametrize("B", [1, 2, 3, 4])
+def test_skinny_adaln_shard_gelu_bias(B):
+    """The adaLN shard at tp 4 (9216 x 6144: 4.5 weight rows per wave, so rows are dealt
+    wave-major), random operands, bias and GELU, bf16 output, against the oracle on a sample
+    of weight rows: every 7th, the rows around 8192 where some waves' fifth rows begin, and
+    the last."""
+    rng = np.random.default_rng(80 + B)
+    N, K = 9216, 6144
+    c = si.normal_bf16(rng, (B, K))
+    w = si.normal_bf16(rng, (N, K), 1 / np.sqrt(K))
+    bb = si.normal_bf16(rng, (N,))
+    y = dev_to_f64(tsl.tp_linear_colwise(bits_to_dev(c), bits_to_dev(w), bits_to_dev(bb), act="gelu_tanh"))
+    cols = np.unique(np.concatenate([np.arange(0, N, 7), np.arange(8 * 1024 - 8, 8 * 1024 + 8), [N - 1]]))
+    ref = oracle.colwise(c, w[cols], bb[cols], act=oracle.ACT_GELU_TANH)
+    check_close(y[:, cols], ref, K, True, S=abs_dot(c, w[cols], bb[cols]), what=f"adaLN shard B={B}")
+
+
 @pytest.mark.parametrize("N", [16, 304, 2048, 2064, 3 * 2048 - 16, 5 * 2048 + 1008])
 def test_skinny_rows_per_wave(N):
     """Rows per wave from one (a grid smaller than the chip) to six, so that every peeled ending
