@@ -1167,6 +1167,52 @@ def configs_bench(args):
     y = torch.empty(M, D, dtype=torch.float32, device=dev)
     call("tiny_mlp", f"SUM of {P} x [{M},{D}] f32 + b2", lambda: tsl.tp_partial_combine(
         parts, "sum", bias=a["b2"], out=y), 0, P * 4 * M * D + 4 * M * D + 2 * D)
+
+    # The whole forward (both ranks' GEMMs and the SUM, 2 P + 1 launches) is launch-bound:
+    # launched call by call against one replay of a HIP graph captured from the same calls.
+    def forward():
+        for r in range(P):
+            tsl.tp_linear_colwise(a["x"], w1s[r][0], w1s[r][1], act="gelu_tanh", out=hs[r])
+            tsl.tp_linear_rowwise(hs[r], w2s[r], out=parts[r])
+        tsl.tp_partial_combine(parts, "sum", bias=a["b2"], out=y)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        forward()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        forward()
+    forward()
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(y.view(torch.int32), y_eager.view(torch.int32)):
+        raise SystemExit("tiny MLP: the graph replay differs from the eager forward")
+    def paced_us(fn):
+        """Average of reps calls issued from Python with no spin kernel ahead of them, so the
+        host's launch overhead is timed too (a caller's view of a launch-bound sequence)."""
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    graph_rows = [dict(config="tiny_mlp", call=f"forward, {2 * P + 1} launches (both ranks' GEMMs, SUM)",
+                       eager_us=round(warm_us(forward), 2), graph_us=round(warm_us(graph.replay), 2),
+                       eager_paced_us=round(paced_us(forward), 2), graph_paced_us=round(paced_us(graph.replay), 2))]
+    print(f"# tiny_mlp forward: queued ahead eager {graph_rows[0]['eager_us']} us, graph {graph_rows[0]['graph_us']} us;"
+          f" issued from Python eager {graph_rows[0]['eager_paced_us']} us, graph {graph_rows[0]['graph_paced_us']} us",
+          file=sys.stderr, flush=True)
+    del graph
     oracle_rows.append(_oracle_config("tiny_mlp", wl))
     del a, w1s, w2s, hs, parts
 
@@ -1226,7 +1272,7 @@ def configs_bench(args):
     oracle_rows.append(_oracle_config("adaln", wl))
     del a, wa
 
-    out = {"configs": rows, "cpu_baseline": oracle_rows, "reps": reps, "warmup": warm,
+    out = {"configs": rows, "graph": graph_rows, "cpu_baseline": oracle_rows, "reps": reps, "warmup": warm,
            "cold": f"{FLUSH_BYTES >> 20} MiB read before each call"}
     md = ["| workload | call | bound | cold µs | warm µs | cold rate | % of peak | roofline frac |",
           "|---|---|---|---|---|---|---|---|"]
@@ -1235,6 +1281,16 @@ def configs_bench(args):
         pct = r.get("pct_mfma_peak", r.get("pct_hbm_peak"))
         md.append(f"| {r['config']} | {r['call']} | {r['bound']} | {r['cold_us']} | {r['warm_us']} | {rate} | "
                   f"{pct} | {r['roofline_frac']} |")
+    md += ["", "Short sequences replayed from a HIP graph (warm, per forward; the graph is captured from "
+           "the same library calls and its output checked against them bit for bit).  'Queued ahead': a "
+           "spin kernel first lets the host enqueue every call before the GPU reaches them, so only GPU "
+           "time counts; 'issued from Python': the calls are timed as a Python caller issues them, host "
+           "overhead included.", "",
+           "| workload | sequence | call by call, queued ahead, µs | graph, queued ahead, µs | "
+           "call by call, issued from Python, µs | graph, issued from Python, µs |", "|---|---|---|---|---|---|"]
+    for g in graph_rows:
+        md.append(f"| {g['config']} | {g['call']} | {g['eager_us']} | {g['graph_us']} | {g['eager_paced_us']} | "
+                  f"{g['graph_paced_us']} |")
     md += ["", "| workload | oracle sample | oracle seconds | oracle GFLOP/s | threads |", "|---|---|---|---|---|"]
     for o in oracle_rows:
         md.append(f"| {o['config']} | {o['sample']} | {o['seconds']} | {o['gflops']} | {o['cores']} |")
