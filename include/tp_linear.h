@@ -98,8 +98,11 @@ typedef enum { TP_COMBINE_SUM = 0, TP_COMBINE_CONCAT = 1 } tp_combine;
  *
  * Arithmetic: bf16 products, fp32 accumulation (MFMA), bias and activation in
  * fp32, one rounding to y_dtype (round to nearest even for bf16).
- * Small M (up to 8 rows, K <= 8192) uses a weight-streaming kernel (the skinny adaLN modulation shape),
- * larger M, and SwiGLU at any M, the tiled MFMA kernel; both obey the same contract.
+ * Kernels, all under the same contract: up to 8 rows without SwiGLU (6 for
+ * K > 4096, 2 for K > 6144; K <= 8192) a weight-streaming kernel (the skinny
+ * adaLN modulation shape); other problems with up to 64 rows a split-K MFMA
+ * kernel (all rows and 32 output columns per workgroup); more rows the tiled
+ * MFMA kernel.
  * Requires K % 64 == 0 and n_shard % 16 == 0, each operand view (rows x
  * leading dimension) below 2 GiB, row strides of at most 2^31 elements and
  * at most 2^22 output tiles of 192 x 256 (TP_ERR_UNSUPPORTED otherwise).
@@ -122,7 +125,8 @@ tp_status tp_linear_colwise(const void *x, int64_t ldx, const void *w_shard, int
  *                         weight works the same way)
  *   partial [M, N]        fp32, row stride ldp (>= N, multiple of 4)
  *
- * Arithmetic: bf16 products, fp32 accumulation, fp32 store.
+ * Arithmetic: bf16 products, fp32 accumulation, fp32 store.  Kernels as for
+ * tp_linear_colwise.
  * Requires k_shard % 64 == 0 and N % 16 == 0, each operand view (rows x
  * leading dimension) below 2 GiB, row strides of at most 2^31 elements and
  * at most 2^22 output tiles of 192 x 256 (TP_ERR_UNSUPPORTED otherwise).
@@ -137,8 +141,9 @@ tp_status tp_linear_rowwise(const void *x_shard, int64_t ldx, const void *w_shar
  * features, K input features, activation act; for TP_ACT_SWIGLU, N counts the
  * outputs, not the 2 N weight rows) on the current device: *tile_rows and
  * *tile_cols receive the tiled kernel's output tile (rows 256, 224 or 192;
- * columns 256 or 192, or 128 outputs with SwiGLU), or both 0 when the
- * weight-streaming kernel would run.  The choice depends on the shape and on
+ * columns 256 or 192, or 128 outputs with SwiGLU); for the split-K kernel
+ * (up to 64 rows) 16 ceil(M / 16) rows and 32 columns (16 with SwiGLU); or
+ * both 0 when the weight-streaming kernel would run.  The choice depends on the shape and on
  * the device's compute-unit count.  It lets a caller check results at the
  * tiles' real edges.  No device work, no allocation.
  * Errors: TP_ERR_INVALID_ARG for a null output pointer, an unknown act, or
@@ -162,8 +167,8 @@ tp_status tp_linear_tile_shape(int64_t M, int64_t N, int64_t K, tp_act act, int6
  *   w_shard [N, k_full/P]  bf16, row stride ldw
  *   partial [M, N]         fp32, row stride ldp (>= N, multiple of 4)
  *
- * Arithmetic as tp_linear_rowwise; small M (up to 8 rows, k_full/P <= 8192)
- * uses the weight-streaming kernel.
+ * Arithmetic and kernels as tp_linear_rowwise on the slice (a few rows: the
+ * weight-streaming kernel, up to 64 rows the split-K kernel).
  * Errors (before any device work): TP_ERR_INVALID_ARG for tp_degree < 1 or
  * rank outside [0, tp_degree); TP_ERR_NOT_DIVISIBLE if tp_degree does not
  * divide k_full; then every check of tp_linear_rowwise on the slice.

@@ -1,8 +1,9 @@
 // abi.hip -- the extern "C" entry points of libtp_linear.so (include/tp_linear.h).
 //
 // Each entry point validates every argument before touching the device, turns
-// the request into kernel launches (tiled MFMA GEMM, skinny weight-streaming
-// kernel, bit-exact segment copies, SUM combine) on the caller's stream, and
+// the request into kernel launches (tiled MFMA GEMM, split-K MFMA kernel for
+// up to 64 rows, skinny weight-streaming kernel, bit-exact segment copies, SUM
+// combine) on the caller's stream, and
 // reports errors through a status code plus a thread-local message.  Nothing
 // is allocated and no state is kept between calls.
 #include <stdarg.h>
@@ -95,9 +96,15 @@ tp_status check_linear(const char *fn, const void *x, int64_t ldx, const void *w
 
 tp_status run_linear(const char *fn, const tpl::LinearProblem &p, hipStream_t stream)
 {
-    // The skinny kernel has no gated epilogue: SwiGLU always takes the tiled kernel.
-    const bool skinny = !p.swiglu && tpl::gemv_supports(p.M, p.K);
-    const hipError_t e = skinny ? tpl::launch_gemv(p, stream) : tpl::launch_gemm(p, stream);
+    // The weight-streaming kernel has no gated epilogue: SwiGLU with few rows takes the
+    // split-K kernel.
+    hipError_t e;
+    if (!p.swiglu && tpl::gemv_supports(p.M, p.K))
+        e = tpl::launch_gemv(p, stream);
+    else if (tpl::narrow_supports(p.M))
+        e = tpl::launch_narrow(p, stream);
+    else
+        e = tpl::launch_gemm(p, stream);
     return hip_status(e, fn);
 }
 
@@ -194,7 +201,10 @@ tp_status tp_linear_tile_shape(int64_t M, int64_t N, int64_t K, tp_act act, int6
         return TP_OK;
     }
     int rows = 0, cols = 0;
-    tpl::gemm_tile_shape(p, &rows, &cols);
+    if (tpl::narrow_supports(M))
+        tpl::narrow_tile_shape(p, &rows, &cols);
+    else
+        tpl::gemm_tile_shape(p, &rows, &cols);
     *tile_rows = rows;
     *tile_cols = cols;
     return TP_OK;

@@ -29,7 +29,7 @@ struct LinearProblem {
     bool swiglu = false;  // W holds 2N rows [gate; up]; y = silu(x gate^T + b_g) * (x up^T + b_u)
 };
 
-// Tiled MFMA GEMM (M > kSkinnyMaxM).  Requires K % 64 == 0, N % 16 == 0.
+// Tiled MFMA GEMM (M > kNarrowMaxM).  Requires K % 64 == 0, N % 16 == 0.
 hipError_t launch_gemm(const LinearProblem &p, hipStream_t stream);
 // Output tile launch_gemm picks for p on the current device: rows 256, 224 or 192,
 // columns 256 or 192 (128 outputs with SwiGLU).
@@ -44,6 +44,14 @@ constexpr int64_t kSkinnyMaxK = 8192;
 constexpr int64_t kSkinnyMaxLdsBytes = 96 * 1024;
 bool gemv_supports(int64_t M, int64_t K);
 hipError_t launch_gemv(const LinearProblem &p, hipStream_t stream);
+
+// Split-K MFMA kernel for few rows (M <= kNarrowMaxM) that the weight-streaming
+// kernel does not take: all M rows and 32 output columns (16 with SwiGLU) per
+// workgroup, K split across its waves.  Same requirements as the tiled kernel.
+constexpr int64_t kNarrowMaxM = 64;
+bool narrow_supports(int64_t M);
+void narrow_tile_shape(const LinearProblem &p, int *rows, int *cols);
+hipError_t launch_narrow(const LinearProblem &p, hipStream_t stream);
 
 // Bit-exact strided copies: `rows` rows of `row_bytes` bytes each.
 struct CopySegment {

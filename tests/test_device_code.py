@@ -59,3 +59,13 @@ def test_every_gemm_instance_is_compiled_and_checked(tmp_path):
     kernels = kernel_resources(os.path.join(CSRC, "gemm_bf16.hip"), tmp_path)
     gemm = [n for n, _, _ in kernels if "gemm_bf16_nt_kernel" in n]
     assert len(gemm) == 60, gemm
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc is not installed")
+def test_every_split_k_instance_is_compiled_and_checked(tmp_path):
+    """The split-K kernel for up to 64 rows has 4 row-block counts x 3 epilogues (none,
+    GELU, SwiGLU) x 2 output types x bias or not: 48 instances, none spilling."""
+    kernels = kernel_resources(os.path.join(CSRC, "gemm_narrow.hip"), tmp_path)
+    narrow = [(n, p) for n, p, _ in kernels if "gemm_narrow_kernel" in n]
+    assert len(narrow) == 48, [n for n, _ in narrow]
+    assert all(p == 0 for _, p in narrow)
