@@ -532,21 +532,6 @@ hipError_t launch_variant(const GemmParams &gp, int nxb, int nwb, hipStream_t st
     }
 }
 
-// Compute units of the current device (cached per device).
-int cu_count()
-{
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 256;
-    int n = cached[dev].load(std::memory_order_relaxed);
-    if (n <= 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cached[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
 
 // Tile shape: the one with the least cost = (rounds of tiles over the CUs) x (tile area)
 // x (cost per flop of the shape).  The per-flop factors are measured in the bench step,
@@ -589,6 +574,22 @@ TileChoice pick_tile(int M, int N, int K, bool gated, int cus)
 }
 
 }  // namespace
+
+// Compute units of the current device (cached per device).
+int cu_count()
+{
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 void gemm_tile_shape(const LinearProblem &pr, int *rows, int *cols)
 {

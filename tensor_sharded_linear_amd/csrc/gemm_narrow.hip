@@ -8,10 +8,13 @@
 // only N / 192 workgroups for 256 CUs (9216 x 6144 weight: 97 us at 7 to 64
 // rows).  Here instead:
 //
-//  * a workgroup of 4 waves owns 32 output columns (16 with SwiGLU: 16 gate and
-//    the 16 matching up rows of the packed weight) and all M rows, as
-//    MB = ceil(M / 16) <= 4 blocks of 16 rows, so N / 32 workgroups (288 for
-//    9216 columns) share the CUs;
+//  * a workgroup of 4 waves owns all M rows, as MB = ceil(M / 16) <= 4 blocks
+//    of 16, and a run of output columns (weight rows) sized so that every CU
+//    streams about the same number of weight lines: 9216 columns on 256 CUs
+//    give 256 runs of 36 (three 16-row weight blocks, the last one partial),
+//    where fixed 32-column runs (288 workgroups) left 32 CUs with two and took
+//    29 us at 7 rows instead of 22.5; with SwiGLU a run is up to 16 gate rows
+//    and the matching up rows of the packed weight;
 //  * its waves split K in steps of 64, dealt round-robin (wave w takes steps
 //    w, w + 4, ...), so the 4 waves read neighbouring 128-byte pieces of each
 //    row;
@@ -19,12 +22,12 @@
 //    one L2 request per line it is asked for and keeps a limited number in
 //    flight per CU, so lanes that each fetched their own MFMA fragment (16 rows
 //    x 64 bytes per load) halved the bytes per request and held the weight
-//    stream at 2.4-2.7 TB/s (7 rows: 47 us, now 28 us);
+//    stream at 2.4-2.7 TB/s (7 rows, 32-column runs: 47 us against 28 us);
 //  * a wave passes each step's lines through its own LDS area (one 2 KiB
 //    16 x 64 tile per block, XOR-swizzled) into the fragment layout of
 //    v_mfma_f32_16x16x32_bf16, the weight as the A operand;
-//  * D steps of loads are in flight per wave (4 with one row block, 3 with two,
-//    2 above): no load sits in a conditional block (rows past the end are
+//  * D steps of loads are in flight per wave (6, 4, 3 or 2 as the weight and
+//    activation blocks number 2, 3, 4 or more): no load sits in a conditional block (rows past the end are
 //    clamped to the last row, steps past the end to the last step, and the
 //    extra data is discarded) and the loads go out in step order, so the
 //    compiler's in-order load counting keeps all D in flight;
@@ -33,9 +36,9 @@
 //    thread then applies bias, GELU or SwiGLU and rounding, and stores the 4
 //    consecutive columns its lane holds.
 //
-// Every workgroup reads all of X (M x K) besides its 32 weight rows, so at 64
-// rows the activation is two thirds of the requests: 9216 x 6144 takes 28 us at
-// 7 rows and 48 us at 64 (the weight alone at 8 TB/s: 14 us).
+// Every workgroup reads all of X (M x K) besides its weight rows, so the
+// activation's share of the requests grows with M: 9216 x 6144 takes 22.5 us at
+// 7 rows and 31 us at 64 (the weight alone at 8 TB/s: 14 us).
 #include "tp_internal.h"
 #include <type_traits>
 
@@ -48,7 +51,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kNB = 2;  // 16-row weight blocks per workgroup
+constexpr int kMaxRows = 48;      // weight rows per workgroup (3 blocks of 16)
+constexpr int kMaxGatedRows = 16; // gate rows (and as many up rows) per workgroup
 
 constexpr int kActNone = 0;
 constexpr int kActGelu = 1;
@@ -61,6 +65,7 @@ struct NarrowParams {
     void *y;
     int64_t ldx, ldw, ldy;
     int M, N, K;
+    int rows;  // output columns (weight rows) per workgroup, a multiple of 4
 };
 
 // GELU, tanh form, as in the tiled kernel: g(v) = v / (1 + exp(-2u)),
@@ -87,33 +92,37 @@ __device__ __forceinline__ f32x4 bias4(const uint16_t *b, int n)
 }
 
 // Steps (64 k each) whose loads are in flight per wave: 8 (NB + MB) registers per step.
-template <int MB>
+template <int MB, int NB>
 constexpr int depth()
 {
-    return MB == 1 ? 4 : (MB == 2 ? 3 : 2);
+    return (NB + MB) <= 2 ? 6 : ((NB + MB) == 3 ? 4 : ((NB + MB) == 4 ? 3 : 2));
 }
 
 // LDS: during the k loop each wave's transpose area (one 2 KiB tile of 16 rows x 64 k per
 // block), after it the waves' partial sums (one 16 x 16 fp32 tile per output block).
-template <int MB>
+template <int MB, int NB>
 struct NarrowLds {
     union {
-        bf16x8 xpose[kWaves][kNB + MB][128];
-        f32x4 red[kWaves][MB * kNB][64];
+        bf16x8 xpose[kWaves][NB + MB][128];
+        f32x4 red[kWaves][MB * NB][64];
     };
 };
 
-template <int MB, int ACT, bool OUT_BF16, bool HAS_BIAS>
+// NB 16-row weight blocks cover the workgroup's p.rows weight rows (gated: block 0 the
+// gate rows, block 1 the matching up rows, p.rows <= 16).
+template <int MB, int NB, int ACT, bool OUT_BF16, bool HAS_BIAS>
 __global__ __launch_bounds__(kThreads) void gemm_narrow_kernel(NarrowParams p)
 {
     constexpr bool kGated = ACT == kActSwiglu;
-    constexpr int D = depth<MB>();
-    constexpr int kCols = kGated ? 16 : 16 * kNB;  // output columns per workgroup
-    __shared__ NarrowLds<MB> lds;
+    static_assert(!kGated || NB == 2, "the gated form pairs one gate and one up block");
+    constexpr int kNB = NB;
+    constexpr int D = depth<MB, NB>();
+    __shared__ NarrowLds<MB, NB> lds;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n0 = blockIdx.x * kCols;
+    const int n0 = blockIdx.x * p.rows;
+    const int n_end = min(n0 + p.rows, p.N);  // a multiple of 4
     // Steps of 64 k, dealt round-robin: wave w takes steps w, w + 4, ..., so at any time the
     // 4 waves read neighbouring 128-byte pieces of each row.
     const int steps = ((p.K >> 6) - wave + kWaves - 1) / kWaves;
@@ -125,7 +134,9 @@ __global__ __launch_bounds__(kThreads) void gemm_narrow_kernel(NarrowParams p)
     // it sent 64-byte requests, and the number of requests it keeps in flight per CU held
     // the weight stream to well under half the rate.  Weight rows of block j:
     // n0 + 16 j + 8 h + l / 8 (gated: block 0 the gate rows n0 + ..., block 1 the up rows
-    // N + n0 + ...); activation rows of block i: 16 i + 8 h + l / 8; clamped to the last row.
+    // N + n0 + ...), clamped to the workgroup's last row; activation rows of block i:
+    // 16 i + 8 h + l / 8, clamped to the last row.  Clamped rows repeat a line that the
+    // same load already asks for, which costs no extra request.
     const int lrow = lane >> 3, lchunk = lane & 7;
     const int kofs = wave * 64 + 8 * lchunk;
     const bf16x8 *wp[kNB][2];
@@ -134,8 +145,8 @@ __global__ __launch_bounds__(kThreads) void gemm_narrow_kernel(NarrowParams p)
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int j = 0; j < kNB; ++j) {
-            const int r = kGated ? j * p.N + min(n0 + 8 * h + lrow, p.N - 1)
-                                 : min(n0 + 16 * j + 8 * h + lrow, p.N - 1);
+            const int r = kGated ? j * p.N + min(n0 + 8 * h + lrow, n_end - 1)
+                                 : min(n0 + 16 * j + 8 * h + lrow, n_end - 1);
             wp[j][h] = reinterpret_cast<const bf16x8 *>(p.w + (int64_t)r * p.ldw + kofs);
         }
 #pragma unroll
@@ -244,7 +255,8 @@ __global__ __launch_bounds__(kThreads) void gemm_narrow_kernel(NarrowParams p)
 
     typedef typename std::conditional<OUT_BF16, __bf16, float>::type OutT;
     // Item (block, l): lane l of every wave holds Y[16 i + l % 16][n .. n + 3],
-    // n = column base + 16 j + 4 (l / 16).  N % 16 == 0, so n < N covers n + 3.
+    // n = column base + 16 j + 4 (l / 16).  n and n_end are multiples of 4, so n < n_end
+    // covers n + 3.
     constexpr int kItems = (kGated ? MB : MB * kNB) * 64;
     for (int e = threadIdx.x; e < kItems; e += kThreads) {
         const int l = e & 63;
@@ -255,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void gemm_narrow_kernel(NarrowParams p)
 #pragma unroll
         for (int w = 1; w < kWaves; ++w)
             v += lds.red[w][blk][l];
-        if (m >= p.M || n >= p.N)
+        if (m >= p.M || n >= n_end)
             continue;
         if (HAS_BIAS)
             v += bias4(p.bias, n);
@@ -285,23 +297,36 @@ __global__ __launch_bounds__(kThreads) void gemm_narrow_kernel(NarrowParams p)
     }
 }
 
-template <int MB, int ACT, bool OUT_BF16, bool HAS_BIAS>
+template <int MB, int NB, int ACT, bool OUT_BF16, bool HAS_BIAS>
 hipError_t launch_mb(const NarrowParams &np, hipStream_t stream)
 {
-    const int cols = ACT == kActSwiglu ? 16 : 16 * kNB;
-    hipLaunchKernelGGL((gemm_narrow_kernel<MB, ACT, OUT_BF16, HAS_BIAS>), dim3((np.N + cols - 1) / cols),
+    hipLaunchKernelGGL((gemm_narrow_kernel<MB, NB, ACT, OUT_BF16, HAS_BIAS>), dim3((np.N + np.rows - 1) / np.rows),
                        dim3(kThreads), 0, stream, np);
     return hipGetLastError();
+}
+
+template <int NB, int ACT, bool OUT_BF16, bool HAS_BIAS>
+hipError_t launch_nb(const NarrowParams &np, hipStream_t stream)
+{
+    switch ((np.M + 15) / 16) {
+    case 1: return launch_mb<1, NB, ACT, OUT_BF16, HAS_BIAS>(np, stream);
+    case 2: return launch_mb<2, NB, ACT, OUT_BF16, HAS_BIAS>(np, stream);
+    case 3: return launch_mb<3, NB, ACT, OUT_BF16, HAS_BIAS>(np, stream);
+    default: return launch_mb<4, NB, ACT, OUT_BF16, HAS_BIAS>(np, stream);
+    }
 }
 
 template <int ACT, bool OUT_BF16, bool HAS_BIAS>
 hipError_t launch_act(const NarrowParams &np, hipStream_t stream)
 {
-    switch ((np.M + 15) / 16) {
-    case 1: return launch_mb<1, ACT, OUT_BF16, HAS_BIAS>(np, stream);
-    case 2: return launch_mb<2, ACT, OUT_BF16, HAS_BIAS>(np, stream);
-    case 3: return launch_mb<3, ACT, OUT_BF16, HAS_BIAS>(np, stream);
-    default: return launch_mb<4, ACT, OUT_BF16, HAS_BIAS>(np, stream);
+    if constexpr (ACT == kActSwiglu) {
+        return launch_nb<2, ACT, OUT_BF16, HAS_BIAS>(np, stream);
+    } else {
+        switch ((np.rows + 15) / 16) {
+        case 1: return launch_nb<1, ACT, OUT_BF16, HAS_BIAS>(np, stream);
+        case 2: return launch_nb<2, ACT, OUT_BF16, HAS_BIAS>(np, stream);
+        default: return launch_nb<3, ACT, OUT_BF16, HAS_BIAS>(np, stream);
+        }
     }
 }
 
@@ -315,6 +340,32 @@ hipError_t launch_out(const NarrowParams &np, int act, hipStream_t stream)
     }
 }
 
+// Weight rows per workgroup.  The CUs share the weight stream; a CU's time goes with the
+// lines it requests: its workgroups' weight rows plus, for each workgroup, the activation
+// rows (every workgroup reads all of X; an activation line, served from L2, costs about
+// 0.6 of a weight line from HBM).  Workgroups beyond one per CU run on the same CUs, so the
+// cost of a choice is ceil(workgroups / CUs) x (rows + 0.6 M) (gated: 2 rows per output).
+// Rows are a multiple of 4 (the epilogue stores 4 columns per lane), at most 48 (16 gated).
+// Ties go to more rows per workgroup (fewer activation re-reads).  9216 outputs on 256 CUs
+// take 36 rows: 256 workgroups, one per CU; 32 rows per workgroup left 32 CUs with two.
+int pick_rows(int64_t M, int64_t N, bool gated, int cus)
+{
+    const int max_rows = gated ? kMaxGatedRows : kMaxRows;
+    const double x_cost = 0.6 * (double)M;
+    int best = 4;
+    double best_cost = -1;
+    for (int rows = 4; rows <= max_rows; rows += 4) {
+        const int64_t wgs = (N + rows - 1) / rows;
+        const int64_t rounds = (wgs + cus - 1) / cus;
+        const double cost = (double)rounds * ((gated ? 2 : 1) * rows + x_cost);
+        if (best_cost < 0 || cost <= best_cost) {
+            best = rows;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
 }  // namespace
 
 bool narrow_supports(int64_t M) { return M >= 1 && M <= kNarrowMaxM; }
@@ -322,7 +373,7 @@ bool narrow_supports(int64_t M) { return M >= 1 && M <= kNarrowMaxM; }
 void narrow_tile_shape(const LinearProblem &pr, int *rows, int *cols)
 {
     *rows = (int)(16 * ((pr.M + 15) / 16));
-    *cols = pr.swiglu ? 16 : 16 * kNB;
+    *cols = pick_rows(pr.M, pr.N, pr.swiglu, cu_count());
 }
 
 hipError_t launch_narrow(const LinearProblem &pr, hipStream_t stream)
@@ -340,6 +391,7 @@ hipError_t launch_narrow(const LinearProblem &pr, hipStream_t stream)
     np.M = (int)pr.M;
     np.N = (int)pr.N;
     np.K = (int)pr.K;
+    np.rows = pick_rows(pr.M, pr.N, pr.swiglu, cu_count());
     const int act = pr.swiglu ? kActSwiglu : (pr.gelu ? kActGelu : kActNone);
     if (pr.out_bf16)
         return pr.bias ? launch_out<true, true>(np, act, stream) : launch_out<true, false>(np, act, stream);

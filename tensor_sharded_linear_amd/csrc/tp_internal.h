@@ -29,6 +29,9 @@ struct LinearProblem {
     bool swiglu = false;  // W holds 2N rows [gate; up]; y = silu(x gate^T + b_g) * (x up^T + b_u)
 };
 
+// Compute units of the current device (cached per device; 256 without a device).
+int cu_count();
+
 // Tiled MFMA GEMM (M > kNarrowMaxM).  Requires K % 64 == 0, N % 16 == 0.
 hipError_t launch_gemm(const LinearProblem &p, hipStream_t stream);
 // Output tile launch_gemm picks for p on the current device: rows 256, 224 or 192,

@@ -292,13 +292,16 @@ def test_tile_shape_query():
     library assumes 256 compute units, MI355X's count."""
     q = tsl.tp_linear_tile_shape
     assert q(4, 9216, 6144) == (0, 0)                     # adaLN rows: weight-streaming kernel
-    assert q(4, 9216, 6144, "swiglu") == (16, 16)         # no gated epilogue there: split-K kernel
-    assert q(6, 9216, 6144) == (0, 0) and q(7, 9216, 6144) == (16, 32)   # skinny row limit at 12 chunks
+    assert q(4, 9216, 6144, "swiglu") == (16, 12)         # no gated epilogue there: split-K kernel
+    assert q(6, 9216, 6144) == (0, 0) and q(7, 9216, 6144) == (16, 36)   # skinny row limit at 12 chunks
     assert q(8, 9216, 4096) == (0, 0)                     # 8 chunks: all 8 rows
-    assert q(2, 9216, 8192) == (0, 0) and q(3, 9216, 8192) == (16, 32)   # 16 chunks: 2 rows
-    assert q(9, 9216, 4096) == (16, 32) and q(17, 512, 256) == (32, 32)
-    assert q(64, 512, 256, "gelu_tanh") == (64, 32)       # the tiny MLP's colwise GEMM
-    assert q(64, 272, 1024, "swiglu") == (64, 16)
+    assert q(2, 9216, 8192) == (0, 0) and q(3, 9216, 8192) == (16, 36)   # 16 chunks: 2 rows
+    # split-K kernel: rows per workgroup balance the weight over the 256 CUs
+    assert q(64, 9216, 6144) == (64, 36)                  # 256 workgroups of 36 rows
+    assert q(64, 18432, 6144) == (64, 36)                 # 512: two per CU
+    assert q(64, 4608, 6144) == (64, 20)                  # 231 workgroups
+    assert q(64, 512, 256, "gelu_tanh") == (64, 4)        # the tiny MLP's colwise GEMM
+    assert q(33, 2080, 128, "swiglu") == (48, 12)
     assert q(65, 9216, 6144)[0] in (192, 224, 256)        # past 64 rows: tiled kernel
     assert q(4608, 2304, 6144) == (224, 192)              # 252 tiles, one round
     assert q(4608, 4608, 6144, "gelu_tanh") == (224, 192)  # 504 tiles, 1.97 rounds

@@ -3,12 +3,15 @@
 through the C ABI.
 
 The kernel gives each workgroup all M rows (16-row MFMA blocks, the last one
-partial) and 32 output columns (16 with SwiGLU), splits K over its 4 waves
-(K / 32 steps, unevenly when 4 does not divide them, none at all for some waves
-when K = 64), and adds the 4 partial sums in wave order.  The shapes below
-reach every row-block count with full and partial last blocks, a last
-workgroup with 16 of its 32 columns, all three epilogues, both output types
-and strided operands.  Integer-valued inputs make every summation order exact:
+partial) and a run of output columns (weight rows) that the host sizes to
+balance the CUs: a multiple of 4, at most 48 (one to three 16-row weight blocks,
+the last one partial) or 16 with SwiGLU, the last workgroup's run shorter when
+it does not divide N.  K is dealt over the 4 waves in 64-element steps
+(unevenly when 4 does not divide them, none at all for some waves when K = 64),
+and the 4 partial sums are added in wave order.  The shapes below reach every
+row-block count with full and partial last blocks, runs of one, two and three
+weight blocks with and without a shorter last run, all three epilogues, both
+output types and strided operands.  Integer-valued inputs make every summation order exact:
 the GPU must equal the oracle bit for bit, which pins operand layout and
 indexing.  Random inputs are held to the stated tolerance and the derived
 per-element bound.
@@ -29,7 +32,33 @@ SHAPES = [(16, 64), (48, 192), (2064, 448), (304, 6144)]
 
 
 def _narrow(M, N, K, act="none"):
-    return tsl.tp_linear_tile_shape(M, N, K, act=act) == (16 * ((M + 15) // 16), 16 if act == "swiglu" else 32)
+    rows, cols = tsl.tp_linear_tile_shape(M, N, K, act=act)
+    return rows == 16 * ((M + 15) // 16) and cols % 4 == 0 and 4 <= cols <= (16 if act == "swiglu" else 48)
+
+
+# (N, weight rows per workgroup on 256 CUs at K = 128): one, two and three 16-row weight
+# blocks per workgroup, each with N a multiple of the run and not.
+RUNS = [(2080, 12), (4160, 20), (4112, 20), (8208, 36), (8224, 36)]
+
+
+@pytest.mark.parametrize("M", [9, 40, 64])
+@pytest.mark.parametrize("N,run", RUNS)
+def test_narrow_balanced_runs_integer_exact(M, N, run):
+    rng = np.random.default_rng(1500 + M + N)
+    K = 128
+    x = si.int_bf16(rng, (M, K), -3, 3)
+    w = si.int_bf16(rng, (N, K), -3, 3)
+    b = si.int_bf16(rng, (N,), -8, 8)
+    rows, cols = tsl.tp_linear_tile_shape(M, N, K)
+    assert rows == 16 * ((M + 15) // 16)
+    if tsl.tp_linear_tile_shape(4608, 2304, 6144) == (224, 192):   # 256 CUs: the runs listed
+        assert cols == run
+    y = tsl.tp_linear_colwise(bits_to_dev(x), bits_to_dev(w), bits_to_dev(b), act="gelu_tanh",
+                              out_dtype=torch.float32)
+    check_close(dev_to_f64(y), oracle.colwise(x, w, b, act=oracle.ACT_GELU_TANH), K, False,
+                S=abs_dot(x, w, b), what=f"narrow run {M}x{N}")
+    p = tsl.tp_linear_rowwise(bits_to_dev(x), bits_to_dev(w))
+    assert np.array_equal(dev_to_f64(p), oracle.linear(x, w))
 
 
 @pytest.mark.parametrize("M", ROWS)
@@ -113,6 +142,19 @@ def test_narrow_swiglu_vs_oracle(M, bias, out):
                               act="swiglu", out_dtype=dt)
     assert tuple(y.shape) == (M, n)
     check_swiglu(dev_to_f64(y), x, w, b, out == "bf16", what=f"narrow swiglu {M} bias={bias} {out}")
+
+
+@pytest.mark.parametrize("M", [9, 64])
+def test_narrow_swiglu_ragged_runs(M):
+    """2080 outputs: 12 gate rows and 12 up rows per workgroup, the last run shorter."""
+    rng = np.random.default_rng(5200 + M)
+    n, K = 2080, 192
+    x = si.normal_bf16(rng, (M, K))
+    w = si.normal_bf16(rng, (2 * n, K), 1 / np.sqrt(K))
+    b = si.normal_bf16(rng, (2 * n,))
+    assert _narrow(M, n, K, act="swiglu")
+    y = tsl.tp_linear_colwise(bits_to_dev(x), bits_to_dev(w), bits_to_dev(b), act="swiglu")
+    check_swiglu(dev_to_f64(y), x, w, b, True, what=f"narrow swiglu runs {M}")
 
 
 def test_narrow_swiglu_saturated_gate_exact():
