@@ -98,11 +98,11 @@ typedef enum { TP_COMBINE_SUM = 0, TP_COMBINE_CONCAT = 1 } tp_combine;
  *
  * Arithmetic: bf16 products, fp32 accumulation (MFMA), bias and activation in
  * fp32, one rounding to y_dtype (round to nearest even for bf16).
- * Kernels, all under the same contract: up to 8 rows without SwiGLU (6 for
- * K > 4096, 2 for K > 6144; K <= 8192) a weight-streaming kernel (the skinny
- * adaLN modulation shape); other problems with up to 64 rows a split-K MFMA
- * kernel (all rows and 32 output columns per workgroup); more rows the tiled
- * MFMA kernel.
+ * Kernels, all under the same contract: up to 5 rows without SwiGLU (2 for
+ * K > 6144; K <= 8192) a weight-streaming kernel (the skinny adaLN
+ * modulation shape); other problems with up to 64 rows a split-K MFMA kernel
+ * (all rows and a run of at most 48 output columns per workgroup); more rows
+ * the tiled MFMA kernel.
  * Requires K % 64 == 0 and n_shard % 16 == 0, each operand view (rows x
  * leading dimension) below 2 GiB, row strides of at most 2^31 elements and
  * at most 2^22 output tiles of 192 x 256 (TP_ERR_UNSUPPORTED otherwise).

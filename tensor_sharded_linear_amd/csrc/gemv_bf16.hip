@@ -1,9 +1,9 @@
-// gemv_bf16.hip -- weight-streaming kernel for skinny linear layers (M <= 8).
+// gemv_bf16.hip -- weight-streaming kernel for skinny linear layers (M <= 5).
 //
 // The adaLN modulation projection reads a handful of conditioning vectors
 // (one per sample) and a large weight; the Diffusers "Tensor parallelism"
 // page (section "What to leave out") singles it out as the one large
-// standalone projection.  With M of 1..8 the work is a matrix-vector product
+// standalone projection.  With M of 1..5 the work is a matrix-vector product
 // bound by how fast the weight streams from HBM, so it gets its own kernel:
 //
 //  * one persistent 512-thread workgroup per CU stages the M activation rows
@@ -217,13 +217,10 @@ __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(GemvParams p, int o
 template <int NIT, int B>
 hipError_t launch_variant(const GemvParams &gp, bool out_bf16, bool gelu, hipStream_t stream)
 {
+    // At most 5 rows of 6144 + 8 (or 2 of 8192 + 8) elements: within the 64 KiB of dynamic
+    // LDS a launch gets without raising the limit.
     const size_t lds = (size_t)B * (gp.K + 8) * sizeof(uint16_t);
     auto kern = gemv_bf16_kernel<NIT, B>;
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess)
-            return e;
-    }
     // One persistent workgroup per CU (256 CUs), fewer if there are fewer rows.
     int blocks = (gp.N + kWaves - 1) / kWaves;
     if (blocks > 256)
@@ -247,9 +244,13 @@ int chunk_iters(int64_t K)
     return 0;
 }
 
-// Largest row count whose row buffers + activation batch fit the 256-register
-// budget of two waves per SIMD without spilling, per chunk count.
-constexpr int max_rows(int nit) { return nit <= 8 ? 8 : (nit <= 12 ? 6 : 2); }
+// Largest row count this kernel takes, per chunk count: 5, where the split-K
+// MFMA kernel takes over (measured back to back on three rotating weights:
+// 4 rows x 9216 x 6144 19.4 us here against 23.0 there, 6 rows 22.4 against
+// 21.9, 8 rows x 9216 x 4096 16.2 against 14.5); 2 at 16 chunks, where the row
+// buffers and activation batch of more rows would not fit the 256-register
+// budget of two waves per SIMD.
+constexpr int max_rows(int nit) { return nit <= 12 ? 5 : 2; }
 
 template <int NIT, int B>
 hipError_t launch_if_fits(const GemvParams &gp, bool out_bf16, bool gelu, hipStream_t s)
@@ -267,10 +268,7 @@ hipError_t launch_rows(const GemvParams &gp, bool out_bf16, bool gelu, hipStream
     case 2: return launch_if_fits<NIT, 2>(gp, out_bf16, gelu, s);
     case 3: return launch_if_fits<NIT, 3>(gp, out_bf16, gelu, s);
     case 4: return launch_if_fits<NIT, 4>(gp, out_bf16, gelu, s);
-    case 5: return launch_if_fits<NIT, 5>(gp, out_bf16, gelu, s);
-    case 6: return launch_if_fits<NIT, 6>(gp, out_bf16, gelu, s);
-    case 7: return launch_if_fits<NIT, 7>(gp, out_bf16, gelu, s);
-    default: return launch_if_fits<NIT, 8>(gp, out_bf16, gelu, s);
+    default: return launch_if_fits<NIT, 5>(gp, out_bf16, gelu, s);
     }
 }
 

@@ -41,10 +41,11 @@ void gemm_tile_shape(const LinearProblem &p, int *rows, int *cols);
 // Weight-streaming kernel for skinny M (the adaLN modulation shape): each wave
 // holds whole weight rows of up to kSkinnyMaxK elements in registers, and the
 // M activation rows are staged in at most kSkinnyMaxLdsBytes of LDS.
-// gemv_supports() says whether (M, K) fits; other requests use the tiled kernel.
-constexpr int64_t kSkinnyMaxM = 8;
+// gemv_supports() says whether (M, K) fits; other requests use the split-K or
+// the tiled kernel.
+constexpr int64_t kSkinnyMaxM = 5;
 constexpr int64_t kSkinnyMaxK = 8192;
-constexpr int64_t kSkinnyMaxLdsBytes = 96 * 1024;
+constexpr int64_t kSkinnyMaxLdsBytes = 64 * 1024;
 bool gemv_supports(int64_t M, int64_t K);
 hipError_t launch_gemv(const LinearProblem &p, hipStream_t stream);
 

@@ -293,8 +293,8 @@ def test_tile_shape_query():
     q = tsl.tp_linear_tile_shape
     assert q(4, 9216, 6144) == (0, 0)                     # adaLN rows: weight-streaming kernel
     assert q(4, 9216, 6144, "swiglu") == (16, 12)         # no gated epilogue there: split-K kernel
-    assert q(6, 9216, 6144) == (0, 0) and q(7, 9216, 6144) == (16, 36)   # skinny row limit at 12 chunks
-    assert q(8, 9216, 4096) == (0, 0)                     # 8 chunks: all 8 rows
+    assert q(5, 9216, 6144) == (0, 0) and q(6, 9216, 6144) == (16, 36)   # skinny row limit: 5
+    assert q(5, 9216, 4096) == (0, 0) and q(8, 9216, 4096) == (16, 36)
     assert q(2, 9216, 8192) == (0, 0) and q(3, 9216, 8192) == (16, 36)   # 16 chunks: 2 rows
     # split-K kernel: rows per workgroup balance the weight over the 256 CUs
     assert q(64, 9216, 6144) == (64, 36)                  # 256 workgroups of 36 rows

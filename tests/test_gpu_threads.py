@@ -1,10 +1,9 @@
 """Several host threads calling the library at once, each on its own HIP stream.
 
 The entry points keep per-thread error state and a per-device cache of the compute-unit
-count, and the weight-streaming kernel sets its dynamic LDS size on first use; none of this
-may mix up concurrent callers.  Each thread runs a fixed sequence (a colwise GEMM with GELU,
-a rowwise partial, a 6-row skinny call with more than 64 KiB of staged activations, a SUM
-and an invalid call) several times; every result must equal the same sequence run alone on
+count; none of this may mix up concurrent callers.  Each thread runs a fixed sequence (a
+colwise GEMM with GELU, a rowwise partial, a 5-row weight-streaming call with 60 KiB of
+staged activations, an 8-row split-K call, a SUM and an invalid call) several times; every result must equal the same sequence run alone on
 the default stream, bit for bit, and each thread must see its own error message."""
 import threading
 
@@ -25,7 +24,7 @@ def _inputs(seed):
     w = bits_to_dev(si.normal_bf16(rng, (512, 1024), 1 / 32))
     w2 = bits_to_dev(si.normal_bf16(rng, (256, 512), 1 / 23))
     b = bits_to_dev(si.normal_bf16(rng, (512,)))
-    c = bits_to_dev(si.normal_bf16(rng, (6, 6144)))
+    c = bits_to_dev(si.normal_bf16(rng, (8, 6144)))
     wa = bits_to_dev(si.normal_bf16(rng, (1024, 6144), 1 / 78))
     return x, w, w2, b, c, wa
 
@@ -37,9 +36,10 @@ def _sequence(inp, stream):
         p0 = tsl.tp_linear_rowwise(h, w2, stream=stream)
         p1 = tsl.tp_linear_rowwise(h, w2.flip(0).contiguous(), stream=stream)
         s = tsl.tp_partial_combine([p0, p1], "sum", stream=stream)
-        y = tsl.tp_linear_colwise(c, wa, stream=stream)   # 6 rows x 6144: 73.8 KiB of LDS
+        y = tsl.tp_linear_colwise(c[:5], wa, stream=stream)   # 5 rows x 6144: 60 KiB of LDS
+        z = tsl.tp_linear_colwise(c, wa, act="gelu_tanh", stream=stream)   # 8 rows: split-K
     stream.synchronize()
-    return [t.clone() for t in (h, p0, s, y)]
+    return [t.clone() for t in (h, p0, s, y, z)]
 
 
 def test_concurrent_threads_on_separate_streams():
