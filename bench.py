@@ -92,6 +92,9 @@ def parse():
     ap.add_argument("--configs-trace", metavar="TRACE_CSV",
                     help="no GPU: from the rocprofv3 kernel trace of a --configs run, print per-kernel medians "
                          "of the dispatches right after the cache-flush read (cold) and of the others (warm)")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="RUN_DIR",
+                    help="no GPU: average every counter of rocprofv3 --pmc runs per kernel of this library "
+                         "(name and grid) and print a markdown table")
     return ap.parse_args()
 
 
@@ -621,6 +624,9 @@ def main():
         return
     if args.configs_trace:
         configs_trace(args.configs_trace)
+        return
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
         return
     if args.cold_trace:
         cold_trace(*args.cold_trace)
@@ -1307,6 +1313,11 @@ FAMILY_KERNEL = {"slice": "copy_segments_kernel", "concat": "copy_segments_kerne
 VENDOR_SHAPES = [("colwise", 4608, 2304, 6144), ("colwise", 4608, 4608, 6144), ("colwise", 4608, 9216, 6144),
                  ("rowwise", 4608, 6144, 768), ("rowwise", 4608, 6144, 1536), ("rowwise", 4608, 6144, 2304),
                  ("rowwise", 4608, 6144, 3072), ("rowwise", 4608, 6144, 4608), ("rowwise", 4608, 6144, 9216)]
+# Few token rows: the adaLN shard's weight (9216 x 6144) and the tp 4 rowwise_split_input
+# shard (36864 x 1536) at 1-64 rows, the tiny MLP's two GEMMs, and 128-512 rows (tiled kernel).
+FEW_ROW_SHAPES = ([("colwise", m, 9216, 6144) for m in (1, 4, 6, 16, 32, 64, 128, 512)]
+                  + [("colwise", 64, 18432, 6144), ("rowwise", 8, 36864, 1536), ("rowwise", 64, 6144, 1536),
+                     ("colwise", 64, 512, 256), ("rowwise", 64, 256, 512)])
 
 
 def vendor_bench(args):
@@ -1327,6 +1338,11 @@ def vendor_bench(args):
     def timed(fn):
         for i in range(warm):
             fn(i % 3)
+        torch.cuda.synchronize()
+        # A 1 ms spin first: the host enqueues all reps calls before the GPU reaches them, so
+        # the pair times the GPU work back to back, not the host's launch rate (which bounds
+        # the few-microsecond products otherwise).
+        torch.cuda._sleep(2_000_000)
         e0, e1 = TimingEvent(), TimingEvent()
         e0.record(stream)
         for i in range(reps):
@@ -1339,7 +1355,8 @@ def vendor_bench(args):
         return us
 
     rows = []
-    for kind, M, N, K in VENDOR_SHAPES:
+    shapes = [(s, "step") for s in VENDOR_SHAPES] + [(s, "few") for s in FEW_ROW_SHAPES]
+    for (kind, M, N, K), group in shapes:
         g = torch.Generator(device=dev)
         g.manual_seed(M * 7 + N * 3 + K)
         xs = [torch.randn(M, K, device=dev, generator=g).to(torch.bfloat16) for _ in range(3)]
@@ -1363,25 +1380,49 @@ def vendor_bench(args):
             t_vend.append(timed(vend))
         a, b = min(t_ours), min(t_vend)
         fl = 2.0 * M * N * K
-        rows.append(dict(kind=kind, shape=f"{M}x{N}x{K}", ours_us=round(a, 1), ours_tflops=round(fl / a / 1e6, 1),
-                         vendor_us=round(b, 1), vendor_tflops=round(fl / b / 1e6, 1), vendor=vend_note,
+        rows.append(dict(group=group, kind=kind, shape=f"{M}x{N}x{K}", ours_us=round(a, 1),
+                         ours_tflops=round(fl / a / 1e6, 1), ours_gbs=round(2.0 * N * K / a / 1e3),
+                         vendor_us=round(b, 1), vendor_tflops=round(fl / b / 1e6, 1), vendor_gbs=round(2.0 * N * K / b / 1e3),
+                         vendor=vend_note,
                          tile=tsl.tp_linear_tile_shape(M, N, K)))
         print(f"# {kind} {M}x{N}x{K}: ours {a:.1f} us, vendor {b:.1f} us", file=sys.stderr, flush=True)
         del xs, ws
-    md = ["# GEMM shapes of the step: this library against the vendor BLAS (hipBLASLt)", "",
+    md = ["# GEMM shapes: this library against the vendor BLAS (hipBLASLt)", "",
           "Command (run from the repository root on one MI355X):", "", "```",
           "python3 bench.py " + " ".join(sys.argv[1:]), "```", "",
           "Plain products without bias or activation, the shapes of the step's GEMMs (M x N x K: tokens x "
-          "output features x input features).  Each figure: 3 warm-up calls, then 20 calls back to back on "
-          "three rotating operand sets (random normal bf16) under one event pair, so dispatch gaps are "
-          "included as in the step; the two implementations alternate twice per shape, and the faster "
+          "output features x input features).  Each figure: 3 warm-up calls, then a 1 ms spin kernel and "
+          "20 calls back to back on three rotating operand sets (random normal bf16) under one event pair "
+          "(the spin lets the host queue every call first, so dispatch gaps are included as in the step "
+          "but host launch time is not); the two implementations alternate twice per shape, and the faster "
           "measurement of each is kept.  Percent of the 2.5 PFLOP/s bf16 dense peak.", "",
           "| product | M x N x K | this library (tile) | µs | TFLOP/s | % | vendor | µs | TFLOP/s | % | vendor / library time |",
           "|---|---|---|---|---|---|---|---|---|---|---|"]
+    def kernel_of(r):
+        t0, t1 = r["tile"]
+        if (t0, t1) == (0, 0):
+            return "weight-streaming"
+        return f"split-K, {t1} columns" if t0 <= 64 else f"tiled {t0}x{t1}"
+
     for r in rows:
+        if r["group"] != "step":
+            continue
         md.append(f"| {r['kind']} | {r['shape']} | {r['tile'][0]}x{r['tile'][1]} | {r['ours_us']} | "
                   f"{r['ours_tflops']:.0f} | {100 * r['ours_tflops'] / PEAK_BF16_TFLOPS:.1f} | {r['vendor']} | "
                   f"{r['vendor_us']} | {r['vendor_tflops']:.0f} | {100 * r['vendor_tflops'] / PEAK_BF16_TFLOPS:.1f} | "
+                  f"{r['vendor_us'] / r['ours_us']:.3f} |")
+    md += ["", "## Few token rows", "",
+           "The same measurement for products with 1 to 512 rows: the weight (2 N K bytes) dominates "
+           "the traffic, so the rate is given as weight GB/s against the 8 TB/s HBM peak.  Three "
+           "rotating operand sets take 340 MB and more for the 9216 x 6144 weight, beyond the "
+           "256 MB Infinity Cache.", "",
+           "| product | M x N x K | this library (kernel) | µs | weight GB/s | % of 8 TB/s | vendor µs | "
+           "weight GB/s | vendor / library time |", "|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        if r["group"] != "few":
+            continue
+        md.append(f"| {r['kind']} | {r['shape']} | {kernel_of(r)} | {r['ours_us']} | {r['ours_gbs']} | "
+                  f"{r['ours_gbs'] / 80:.1f} | {r['vendor_us']} | {r['vendor_gbs']} | "
                   f"{r['vendor_us'] / r['ours_us']:.3f} |")
     with open(args.vendor, "w") as f:
         f.write("\n".join(md) + "\n")
@@ -1437,6 +1478,40 @@ def cold_trace(trace_csv, cold_md):
     for fam, (bb, t) in sorted(fam_tot.items()):
         out.append(f"| {fam} | {bb / t / 1e9:.0f} | {100 * bb / t / 1e9 / PEAK_HBM_GBS:.1f} |")
     print("\n".join(out))
+
+
+def pmc_summary(dirs):
+    """Per kernel of this library (short name and grid size), the mean of every counter over its
+    dispatches, across one or more rocprofv3 --pmc run directories (one counter set each)."""
+    import csv
+    import glob
+
+    acc = {}   # (kernel, grid) -> counter -> [values]
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            per = {}
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    short = r["Kernel_Name"].replace("void ", "").replace("tpl::(anonymous namespace)::", "")
+                    short = short.split("(")[0]
+                    if not short.startswith(("gemm_", "gemv_", "copy_", "combine_")):
+                        continue
+                    key = (short, int(r["Grid_Size"]), int(r["Dispatch_Id"]))
+                    per.setdefault(key, {})
+                    per[key][r["Counter_Name"]] = per[key].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            for (k, grid, _), cnt in per.items():
+                e = acc.setdefault((k, grid), {})
+                for c, v in cnt.items():
+                    e.setdefault(c, []).append(v)
+    if not acc:
+        raise SystemExit("no counter_collection.csv with this library's kernels under " + " ".join(dirs))
+    names = sorted({c for e in acc.values() for c in e})
+    print("| kernel | grid (threads) | dispatches | " + " | ".join(names) + " |")
+    print("|---|---|---|" + "---|" * len(names))
+    for (k, grid), e in sorted(acc.items()):
+        n = max(len(v) for v in e.values())
+        vals = [f"{sum(e[c]) / len(e[c]):.0f}" if c in e else "-" for c in names]
+        print(f"| `{k}` | {grid} | {n} | " + " | ".join(vals) + " |")
 
 
 def configs_trace(path):

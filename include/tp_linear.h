@@ -100,7 +100,7 @@ typedef enum { TP_COMBINE_SUM = 0, TP_COMBINE_CONCAT = 1 } tp_combine;
  * fp32, one rounding to y_dtype (round to nearest even for bf16).
  * Kernels, all under the same contract: up to 5 rows without SwiGLU (2 for
  * K > 6144; K <= 8192) a weight-streaming kernel (the skinny adaLN
- * modulation shape); other problems with up to 64 rows a split-K MFMA kernel
+ * modulation shape); other problems with up to 128 rows a split-K MFMA kernel
  * (all rows and a run of at most 48 output columns per workgroup); more rows
  * the tiled MFMA kernel.
  * Requires K % 64 == 0 and n_shard % 16 == 0, each operand view (rows x
@@ -142,7 +142,9 @@ tp_status tp_linear_rowwise(const void *x_shard, int64_t ldx, const void *w_shar
  * outputs, not the 2 N weight rows) on the current device: *tile_rows and
  * *tile_cols receive the tiled kernel's output tile (rows 256, 224 or 192;
  * columns 256 or 192, or 128 outputs with SwiGLU); for the split-K kernel
- * (up to 64 rows) 16 ceil(M / 16) rows and 32 columns (16 with SwiGLU); or
+ * (up to 128 rows) 16 ceil(M / 16) rows (a multiple of 16, 96 for 65-96
+ * rows, 128 above) and the run of 4 to 48 output columns (at most 16 with
+ * SwiGLU) that each workgroup owns; or
  * both 0 when the weight-streaming kernel would run.  The choice depends on the shape and on
  * the device's compute-unit count.  It lets a caller check results at the
  * tiles' real edges.  No device work, no allocation.
@@ -168,7 +170,7 @@ tp_status tp_linear_tile_shape(int64_t M, int64_t N, int64_t K, tp_act act, int6
  *   partial [M, N]         fp32, row stride ldp (>= N, multiple of 4)
  *
  * Arithmetic and kernels as tp_linear_rowwise on the slice (a few rows: the
- * weight-streaming kernel, up to 64 rows the split-K kernel).
+ * weight-streaming kernel, up to 128 rows the split-K kernel).
  * Errors (before any device work): TP_ERR_INVALID_ARG for tp_degree < 1 or
  * rank outside [0, tp_degree); TP_ERR_NOT_DIVISIBLE if tp_degree does not
  * divide k_full; then every check of tp_linear_rowwise on the slice.

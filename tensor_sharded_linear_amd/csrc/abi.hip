@@ -2,7 +2,7 @@
 //
 // Each entry point validates every argument before touching the device, turns
 // the request into kernel launches (tiled MFMA GEMM, split-K MFMA kernel for
-// up to 64 rows, skinny weight-streaming kernel, bit-exact segment copies, SUM
+// up to 128 rows, skinny weight-streaming kernel, bit-exact segment copies, SUM
 // combine) on the caller's stream, and
 // reports errors through a status code plus a thread-local message.  Nothing
 // is allocated and no state is kept between calls.

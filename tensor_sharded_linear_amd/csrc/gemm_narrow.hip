@@ -1,15 +1,15 @@
 // gemm_narrow.hip -- split-K MFMA kernel for linear layers with few rows.
 //
-// Between the weight-streaming kernel's row limit and 64 rows (a small batch of
+// Between the weight-streaming kernel's row limit and 128 rows (a small batch of
 // tokens: a short text stream, the tiny MLP's 64 tokens, adaLN inputs past the
 // weight-streaming kernel's limit), Y = X . W^T moves the whole weight for 2 M
 // flops per weight element, so the weight stream, not the matrix cores, sets
 // the time.  The tiled GEMM's 192-row tiles would be mostly padding and give
-// only N / 192 workgroups for 256 CUs (9216 x 6144 weight: 97 us at 7 to 64
-// rows).  Here instead:
+// only N / 192 workgroups for 256 CUs (9216 x 6144 weight: 97-103 us at 7 to
+// 128 rows).  Here instead:
 //
-//  * a workgroup of 4 waves owns all M rows, as MB = ceil(M / 16) <= 4 blocks
-//    of 16, and a run of output columns (weight rows) sized so that every CU
+//  * a workgroup of 4 waves owns all M rows, as MB = ceil(M / 16) <= 8 blocks
+//    of 16 (6 for 5 blocks, 8 for 7), and a run of output columns (weight rows) sized so that every CU
 //    streams about the same number of weight lines: 9216 columns on 256 CUs
 //    give 256 runs of 36 (three 16-row weight blocks, the last one partial),
 //    where fixed 32-column runs (288 workgroups) left 32 CUs with two and took
@@ -38,7 +38,9 @@
 //
 // Every workgroup reads all of X (M x K) besides its weight rows, so the
 // activation's share of the requests grows with M: 9216 x 6144 takes 22.5 us at
-// 7 rows and 31 us at 64 (the weight alone at 8 TB/s: 14 us).
+// 7 rows, 31 us at 64 and 46 us at 128 (the weight alone at 8 TB/s: 14 us).
+// Beyond 128 rows the activation's re-reads would outweigh the weight, and the
+// tiled kernel takes over.
 #include "tp_internal.h"
 #include <type_traits>
 
@@ -92,10 +94,12 @@ __device__ __forceinline__ f32x4 bias4(const uint16_t *b, int n)
 }
 
 // Steps (64 k each) whose loads are in flight per wave: 8 (NB + MB) registers per step.
+// From 8 blocks on (up to 3 weight and 8 activation blocks) one step, the registers of a
+// second going to the accumulators; the other waves of the CU keep the loads going.
 template <int MB, int NB>
 constexpr int depth()
 {
-    return (NB + MB) <= 2 ? 6 : ((NB + MB) == 3 ? 4 : ((NB + MB) == 4 ? 3 : 2));
+    return (NB + MB) <= 2 ? 6 : ((NB + MB) == 3 ? 4 : ((NB + MB) == 4 ? 3 : ((NB + MB) <= 7 ? 2 : 1)));
 }
 
 // LDS: during the k loop each wave's transpose area (one 2 KiB tile of 16 rows x 64 k per
@@ -312,7 +316,10 @@ hipError_t launch_nb(const NarrowParams &np, hipStream_t stream)
     case 1: return launch_mb<1, NB, ACT, OUT_BF16, HAS_BIAS>(np, stream);
     case 2: return launch_mb<2, NB, ACT, OUT_BF16, HAS_BIAS>(np, stream);
     case 3: return launch_mb<3, NB, ACT, OUT_BF16, HAS_BIAS>(np, stream);
-    default: return launch_mb<4, NB, ACT, OUT_BF16, HAS_BIAS>(np, stream);
+    case 4: return launch_mb<4, NB, ACT, OUT_BF16, HAS_BIAS>(np, stream);
+    case 5:
+    case 6: return launch_mb<6, NB, ACT, OUT_BF16, HAS_BIAS>(np, stream);
+    default: return launch_mb<8, NB, ACT, OUT_BF16, HAS_BIAS>(np, stream);
     }
 }
 
@@ -372,7 +379,8 @@ bool narrow_supports(int64_t M) { return M >= 1 && M <= kNarrowMaxM; }
 
 void narrow_tile_shape(const LinearProblem &pr, int *rows, int *cols)
 {
-    *rows = (int)(16 * ((pr.M + 15) / 16));
+    const int mb = (int)((pr.M + 15) / 16);
+    *rows = 16 * (mb == 5 ? 6 : (mb == 7 ? 8 : mb));  // the instance launch_nb picks
     *cols = pick_rows(pr.M, pr.N, pr.swiglu, cu_count());
 }
 

@@ -63,10 +63,10 @@ def test_every_gemm_instance_is_compiled_and_checked(tmp_path):
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc is not installed")
 def test_every_split_k_instance_is_compiled_and_checked(tmp_path):
-    """The split-K kernel for up to 64 rows has 4 row-block counts x 2 output types x bias
-    or not, times 1-3 weight blocks for each of the 2 plain epilogues (none, GELU) and 2
-    (gate, up) for SwiGLU: 112 instances, none spilling."""
+    """The split-K kernel for up to 128 rows has 6 row-block counts (1-4, 6, 8) x 2 output
+    types x bias or not, times 1-3 weight blocks for each of the 2 plain epilogues (none,
+    GELU) and 2 (gate, up) for SwiGLU: 168 instances, none spilling."""
     kernels = kernel_resources(os.path.join(CSRC, "gemm_narrow.hip"), tmp_path)
     narrow = [(n, p) for n, p, _ in kernels if "gemm_narrow_kernel" in n]
-    assert len(narrow) == 112, [n for n, _ in narrow]
+    assert len(narrow) == 168, [n for n, _ in narrow]
     assert all(p == 0 for _, p in narrow)

@@ -1,5 +1,5 @@
 """GPU parity of the split-K MFMA kernel that runs linear layers with few rows
-(up to 64, beyond the weight-streaming kernel's row limit) against the oracle,
+(up to 128, beyond the weight-streaming kernel's row limit) against the oracle,
 through the C ABI.
 
 The kernel gives each workgroup all M rows (16-row MFMA blocks, the last one
@@ -27,13 +27,19 @@ from helpers import abs_dot, bits_to_dev, check_close, check_swiglu, dev_to_f64
 
 pytestmark = pytest.mark.gpu
 
-ROWS = [9, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64]
+ROWS = [9, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64, 65, 80, 96, 97, 112, 127, 128]
 SHAPES = [(16, 64), (48, 192), (2064, 448), (304, 6144)]
+
+
+def _row_blocks(M):
+    """16-row blocks of the kernel instance for M rows: 1-4, then 6 and 8."""
+    mb = (M + 15) // 16
+    return {5: 6, 7: 8}.get(mb, mb)
 
 
 def _narrow(M, N, K, act="none"):
     rows, cols = tsl.tp_linear_tile_shape(M, N, K, act=act)
-    return rows == 16 * ((M + 15) // 16) and cols % 4 == 0 and 4 <= cols <= (16 if act == "swiglu" else 48)
+    return rows == 16 * _row_blocks(M) and cols % 4 == 0 and 4 <= cols <= (16 if act == "swiglu" else 48)
 
 
 # (N, weight rows per workgroup on 256 CUs at K = 128): one, two and three 16-row weight
@@ -41,7 +47,7 @@ def _narrow(M, N, K, act="none"):
 RUNS = [(2080, 12), (4160, 20), (4112, 20), (8208, 36), (8224, 36)]
 
 
-@pytest.mark.parametrize("M", [9, 40, 64])
+@pytest.mark.parametrize("M", [9, 40, 64, 100, 128])
 @pytest.mark.parametrize("N,run", RUNS)
 def test_narrow_balanced_runs_integer_exact(M, N, run):
     rng = np.random.default_rng(1500 + M + N)
@@ -50,7 +56,7 @@ def test_narrow_balanced_runs_integer_exact(M, N, run):
     w = si.int_bf16(rng, (N, K), -3, 3)
     b = si.int_bf16(rng, (N,), -8, 8)
     rows, cols = tsl.tp_linear_tile_shape(M, N, K)
-    assert rows == 16 * ((M + 15) // 16)
+    assert rows == 16 * _row_blocks(M)
     if tsl.tp_linear_tile_shape(4608, 2304, 6144) == (224, 192):   # 256 CUs: the runs listed
         assert cols == run
     y = tsl.tp_linear_colwise(bits_to_dev(x), bits_to_dev(w), bits_to_dev(b), act="gelu_tanh",
@@ -87,7 +93,7 @@ def test_narrow_rows_past_the_weight_streaming_limit(M):
     assert np.array_equal(dev_to_f64(y), oracle.bf16_widen(oracle.bf16_round(ref)))
 
 
-@pytest.mark.parametrize("M", [9, 33, 64])
+@pytest.mark.parametrize("M", [9, 33, 64, 90, 128])
 @pytest.mark.parametrize("act", ["none", "gelu_tanh"])
 def test_narrow_random_bf16_out(M, act):
     rng = np.random.default_rng(3000 + M)
@@ -112,7 +118,7 @@ def test_narrow_gelu_f32_out_no_bias(M):
                 what=f"narrow gelu f32 {M}")
 
 
-@pytest.mark.parametrize("M", [9, 40, 64])
+@pytest.mark.parametrize("M", [9, 40, 64, 111])
 def test_narrow_rowwise_strided_slices_exact(M):
     """Rowwise partials from column slices of the activation (ldx = 2 K) on
     integer inputs: exact."""
@@ -128,7 +134,7 @@ def test_narrow_rowwise_strided_slices_exact(M):
         assert np.array_equal(dev_to_f64(p), oracle.rowwise(x, r, P, oracle.shard_rowwise(w, P, r)))
 
 
-@pytest.mark.parametrize("M", [9, 33, 64])
+@pytest.mark.parametrize("M", [9, 33, 64, 128])
 @pytest.mark.parametrize("bias,out", [(False, "bf16"), (True, "bf16"), (True, "f32")])
 def test_narrow_swiglu_vs_oracle(M, bias, out):
     rng = np.random.default_rng(5000 + M)
@@ -144,7 +150,7 @@ def test_narrow_swiglu_vs_oracle(M, bias, out):
     check_swiglu(dev_to_f64(y), x, w, b, out == "bf16", what=f"narrow swiglu {M} bias={bias} {out}")
 
 
-@pytest.mark.parametrize("M", [9, 64])
+@pytest.mark.parametrize("M", [9, 64, 81])
 def test_narrow_swiglu_ragged_runs(M):
     """2080 outputs: 12 gate rows and 12 up rows per workgroup, the last run shorter."""
     rng = np.random.default_rng(5200 + M)
@@ -170,12 +176,12 @@ def test_narrow_swiglu_saturated_gate_exact():
     assert np.array_equal(dev_to_f64(y), oracle.linear(x, g) * oracle.linear(x, u))
 
 
-@pytest.mark.parametrize("P", [2, 4])
-def test_narrow_concat_of_shards_equals_unsharded(P):
-    """Each output is the same sum whatever N is: the shards' outputs placed side by
-    side equal the unsharded product bit for bit (random inputs)."""
-    rng = np.random.default_rng(6000 + P)
-    M, N, K = 48, 1024, 768
+@pytest.mark.parametrize("P,M", [(2, 48), (4, 48), (4, 120)])
+def test_narrow_concat_of_shards_equals_unsharded(P, M):
+    """Each output is the same sum whatever N and the run length are: the shards' outputs
+    placed side by side equal the unsharded product bit for bit (random inputs)."""
+    rng = np.random.default_rng(6000 + P + M)
+    N, K = 1024, 768
     x = bits_to_dev(si.normal_bf16(rng, (M, K)))
     w = bits_to_dev(si.normal_bf16(rng, (N, K), 1 / np.sqrt(K)))
     b = bits_to_dev(si.normal_bf16(rng, (N,)))
@@ -204,11 +210,12 @@ def test_narrow_output_view_and_padded_strides():
     assert np.all(got[:, :16] == 7.0) and np.all(got[:, 16 + N:] == 7.0)
 
 
-def test_narrow_adaln_width_random_vs_oracle():
-    """64 rows against the adaLN shard's width (9216 x 6144, 113 MB of weight): every
-    output against the oracle."""
-    rng = np.random.default_rng(7000)
-    M, N, K = 64, 9216, 6144
+@pytest.mark.parametrize("M", [64, 128])
+def test_narrow_adaln_width_random_vs_oracle(M):
+    """64 and 128 rows against the adaLN shard's width (9216 x 6144, 113 MB of weight):
+    every output against the oracle."""
+    rng = np.random.default_rng(7000 + M)
+    N, K = 9216, 6144
     x = si.normal_bf16(rng, (M, K))
     w = si.normal_bf16(rng, (N, K), 1 / np.sqrt(K))
     b = si.normal_bf16(rng, (N,))

@@ -5,7 +5,7 @@ large AdaLN modulation projection is sharded this way): the input is the same
 on every rank, each rank cuts its own slice of the input features, computes an
 fp32 partial with its column block of the weight, and the SUM combine (bias
 added once) rebuilds the unsharded layer.  Skinny inputs (up to 5 rows) run the
-weight-streaming kernel, up to 64 rows the split-K kernel, taller ones the tiled
+weight-streaming kernel, up to 128 rows the split-K kernel, taller ones the tiled
 MFMA kernel.
 """
 import numpy as np

@@ -6,7 +6,7 @@ by the matching up rows, and the rank computes silu(x . gate^T + b_gate) *
 (x . up^T + b_up) for its slice of the hidden features.  The tiled kernel pairs
 gate and up columns inside a tile, so the output is written once, already
 gated.  Ragged shapes span several 128-column output tiles with partial tiles
-on both edges; up to 64 rows the split-K kernel pairs the 16 gate rows and 16
+on both edges; up to 128 rows the split-K kernel pairs the 16 gate rows and 16
 up rows of each 16-column block in one workgroup instead (test_gpu_narrow.py).
 """
 import numpy as np
