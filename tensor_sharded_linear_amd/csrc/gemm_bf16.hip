@@ -517,6 +517,9 @@ template <bool OUT_BF16, bool HAS_BIAS, int ACT>
 hipError_t launch_variant(const GemmParams &gp, int nxb, int nwb, hipStream_t stream)
 {
     if constexpr (ACT != kActSwiglu) {
+        if (nxb == 2)
+            return nwb == 3 ? launch_tm<2, 3, OUT_BF16, HAS_BIAS, ACT>(gp, stream)
+                            : launch_tm<2, 4, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
         if (nwb == 3) {
             switch (nxb) {
             case 6: return launch_tm<6, 3, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
@@ -544,6 +547,11 @@ hipError_t launch_variant(const GemmParams &gp, int nxb, int nwb, hipStream_t st
 // 256 CUs: 4608 x 2304 x 6144 takes 252 tiles of 224 x 192 (one round) instead of 216 of
 // 192 x 256 (119.8 -> 112.2 us in the bench step), 4608 x 4608 x 6144 504 of them (231.7 ->
 // 225.7 us), 4608 x 9216 x 6144 756 of 224 x 256, rowwise 4608 x 6144 x 2304 432 of 256 x 256.
+// 64-row tiles (plain epilogues only) serve a few hundred rows, where the larger tiles leave
+// CUs idle; each of their tiles streams a whole weight panel for 64 rows, so they cost
+// about 2.7 (x 256) and 3.1 (x 192) times a 256 x 256 tile per flop (fitted to back-to-back
+// runs: 256 x 9216 x 6144 took 87 us in 192 tiles of 64 x 192 against 99 us in 96 of
+// 192 x 192; 512 x 3072 x 3072 30 against 39 us).
 struct TileChoice {
     int nxb, nwb;
 };
@@ -554,12 +562,12 @@ TileChoice pick_tile(int M, int N, int K, bool gated, int cus)
         int nxb, nwb;
         double per_flop;
     };
-    static const Cand kCands[6] = {{8, 4, 1.0}, {7, 4, 1.025}, {6, 4, 1.05},
-                                   {8, 3, 1.08}, {7, 3, 1.12}, {6, 3, 1.27}};
+    static const Cand kCands[8] = {{8, 4, 1.0},  {7, 4, 1.025}, {6, 4, 1.05}, {8, 3, 1.08},
+                                   {7, 3, 1.12}, {6, 3, 1.27},  {2, 4, 2.7},  {2, 3, 3.1}};
     TileChoice best{8, 4};
     double best_cost = -1;
     for (const Cand &cd : kCands) {
-        if ((gated && cd.nwb != 4) || (cd.nxb == 7 && K < 3072))
+        if ((gated && (cd.nwb != 4 || cd.nxb == 2)) || (cd.nxb == 7 && K < 3072))
             continue;
         const int bm = 32 * cd.nxb;
         const int cols = cd.nwb == 4 ? (gated ? 128 : 256) : 192;

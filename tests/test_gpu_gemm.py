@@ -3,11 +3,11 @@ kernel for up to 128 rows and the skinny weight-streaming kernel) against the
 oracle, through the C ABI.
 
 Ragged shapes span several tiles with partial tiles on both edges.  The
-kernel picks its tile shape per problem (192, 224 or 256 rows by 192 or 256
-columns, whichever needs the least time in rounds of tiles over the CUs;
+kernel picks its tile shape per problem (64, 192, 224 or 256 rows by 192 or
+256 columns, whichever needs the least time in rounds of tiles over the CUs;
 224 rows only for K >= 3072; tp_linear_tile_shape reports the choice).  On a
 256-CU device the RAGGED shapes with more than 128 rows and the first LARGE one
-run 192 x 192 tiles, the second LARGE one 224 x 192; the RAGGED shapes with 16
+run 64 x 192 tiles, the second LARGE one 224 x 192; the RAGGED shapes with 16
 to 64 rows take the split-K kernel, those with 1 and 5 rows the
 weight-streaming kernel.  TALL runs 224 x 256 tiles (504 in two
 rounds), so its last tile row is ragged inside a tile whose last X DMA

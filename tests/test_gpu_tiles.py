@@ -1,7 +1,8 @@
 """Every tile shape of the tiled GEMM with every epilogue, through the C ABI.
 
 The tiled kernel has one instance per tile shape (192, 224 or 256 rows by 192
-or 256 columns; SwiGLU always 256 weight rows = 128 outputs), output dtype,
+or 256 columns, and 64 rows by 192 or 256 columns for the plain epilogues;
+SwiGLU always 256 weight rows = 128 outputs), output dtype,
 bias or not, and epilogue.  For each shape the library can choose, a problem
 that gets it is found with tp_linear_tile_shape (on the device that runs the
 test, whose compute-unit count the choice depends on), and every instance of
@@ -26,7 +27,7 @@ from helpers import abs_dot, bits_to_dev, check_close, check_swiglu, dev_to_f64,
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(r, c) for r in (256, 224, 192) for c in (256, 192)]
+SHAPES = [(r, c) for r in (256, 224, 192, 64) for c in (256, 192)]
 SUB_ROWS = 160
 
 
