@@ -1315,7 +1315,7 @@ VENDOR_SHAPES = [("colwise", 4608, 2304, 6144), ("colwise", 4608, 4608, 6144), (
                  ("rowwise", 4608, 6144, 3072), ("rowwise", 4608, 6144, 4608), ("rowwise", 4608, 6144, 9216)]
 # Few token rows: the adaLN shard's weight (9216 x 6144) and the tp 4 rowwise_split_input
 # shard (36864 x 1536) at 1-64 rows, the tiny MLP's two GEMMs, and 128-512 rows (tiled kernel).
-FEW_ROW_SHAPES = ([("colwise", m, 9216, 6144) for m in (1, 4, 6, 16, 32, 64, 128, 512)]
+FEW_ROW_SHAPES = ([("colwise", m, 9216, 6144) for m in (1, 4, 6, 16, 32, 64, 128, 256, 512)]
                   + [("colwise", 64, 18432, 6144), ("rowwise", 8, 36864, 1536), ("rowwise", 64, 6144, 1536),
                      ("colwise", 64, 512, 256), ("rowwise", 64, 256, 512)])
 
@@ -1402,7 +1402,7 @@ def vendor_bench(args):
         t0, t1 = r["tile"]
         if (t0, t1) == (0, 0):
             return "weight-streaming"
-        return f"split-K, {t1} columns" if t0 <= 64 else f"tiled {t0}x{t1}"
+        return f"split-K, {t1} columns" if t1 <= 48 else f"tiled {t0}x{t1}"
 
     for r in rows:
         if r["group"] != "step":
