@@ -140,7 +140,7 @@ tp_status tp_linear_rowwise(const void *x_shard, int64_t ldx, const void *w_shar
  * tp_linear_rowwise would run a problem of this shape (M rows, N output
  * features, K input features, activation act; for TP_ACT_SWIGLU, N counts the
  * outputs, not the 2 N weight rows) on the current device: *tile_rows and
- * *tile_cols receive the tiled kernel's output tile (rows 256, 224, 192 or 64;
+ * *tile_cols receive the tiled kernel's output tile (rows 256, 224, 192, 128 or 64;
  * columns 256 or 192, or 128 outputs with SwiGLU); for the split-K kernel
  * (up to 128 rows) 16 ceil(M / 16) rows (a multiple of 16, 96 for 65-96
  * rows, 128 above) and the run of 4 to 48 output columns (at most 16 with

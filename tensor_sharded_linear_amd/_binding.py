@@ -194,7 +194,7 @@ def tp_linear_colwise(x: torch.Tensor, w_shard: torch.Tensor, bias: Optional[tor
 
 def tp_linear_tile_shape(m: int, n: int, k: int, act: str = "none") -> tuple:
     """(rows, cols) of the output tile the tiled kernel uses for an [m, k] x [n, k]^T problem
-    on the current device (rows 256, 224, 192 or 64; cols 256 or 192, 128 with SwiGLU); for the
+    on the current device (rows 256, 224, 192, 128 or 64; cols 256 or 192, 128 with SwiGLU); for the
     split-K kernel (up to 128 rows) (its row blocks x 16, its run of 4 to 48 output columns per
     workgroup, at most 16 with SwiGLU); or (0, 0)
     where the weight-streaming kernel runs.  For ``act="swiglu"`` n counts the outputs.

@@ -93,7 +93,12 @@ struct Tile {
     static constexpr int kDmaX = (BM + 63) / 64;
     static constexpr bool kDmaXPartial = BM % 64 != 0;
     static constexpr int kStageElems = (BM + BN) * BK;  // X tile + W tile
-    static constexpr int kLdsElems = 2 * kStageElems;   // double buffered: 128, 120 or 112 KiB
+    // 64- and 128-row tiles stream a weight panel for few rows and keep more k-tiles in
+    // flight: 64 x 192 4 stages (128 KiB), 64 x 256 3 (120 KiB), 128 x 192 3 (120 KiB),
+    // 128 x 256 3 (144 KiB).  The larger tiles double buffer (128, 120 or 112 KiB): there
+    // the MFMA work of a k-tile covers the loads of the next.
+    static constexpr int kStages = NXB == 2 ? (NWB == 3 ? 4 : 3) : (NXB == 4 ? 3 : 2);
+    static constexpr int kLdsElems = kStages * kStageElems;
     static_assert(BM % 32 == 0, "X tile rows: a multiple of 32");
 };
 
@@ -193,6 +198,26 @@ __device__ __forceinline__ Ctx make_ctx()
 // variant of this kernel compiled with no load wait before its barrier and read
 // stale tiles.
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Waits until at most N of this wave's vector memory instructions are outstanding (they
+// complete in issue order) and its LDS reads have returned: with N = the loads issued
+// after a k-tile's, that k-tile has landed while the later ones stay in flight.
+template <int N>
+__device__ __forceinline__ void wait_dma_keep()
+{
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+}
+
+// A workgroup barrier without the release fence of __syncthreads(), which would wait for
+// every outstanding load, the ones meant to stay in flight included.  The caller waits
+// for what must be complete first; the empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void barrier_only()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // One 16-byte direct-to-LDS load per lane (global_load_lds_dwordx4): lane l
 // writes dst + 16 l bytes.  Kept out of templates: the host pass of a
@@ -316,6 +341,43 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
         __builtin_amdgcn_sched_barrier(0); } while (0)
     const int T = kt1 - kt0;
     Frags<NXB, NWB> f0, f1;
+    if constexpr (L::kStages > 2) {
+        if (T >= L::kStages) {
+            // S stages, k-tile t in stage t % S.  All S are issued first; in iteration t,
+            // once k-tile t + 1 has landed and every wave has read k-tile t, k-tile t + S
+            // goes into k-tile t's stage, so S - 1 k-tiles stay in flight behind the one
+            // being computed.
+            constexpr int S = L::kStages;
+            constexpr int kPer = L::kDmaX + kDmaW;  // DMA instructions per k-tile and wave
+            static_assert(!L::kDmaXPartial, "every wave issues the same loads per k-tile");
+            static_assert((S - 1) * kPer <= 63, "the wait count fits vmcnt");
+            __syncthreads();  // the LDS is free: the previous tile's reads are done
+#pragma unroll
+            for (int i = 0; i < S; ++i)
+                issue(i, i * BK);
+            wait_dma_keep<(S - 1) * kPer>();
+            barrier_only();
+            read_frags(0, 0, f0);
+            int st = 0;
+            for (int t = 0; t < T - 1; ++t) {
+                const int nx = st == S - 1 ? 0 : st + 1;
+                TPL_STEP(read_frags(st, 1, f1), mma(f0));
+                if (t + S - 1 < T)
+                    wait_dma_keep<(S - 2) * kPer>();  // k-tile t + 1 has landed
+                else
+                    wait_dma_keep<0>();
+                barrier_only();
+                if (t + S < T)
+                    issue(st, (t + S) * BK);
+                TPL_STEP(read_frags(nx, 0, f0), mma(f1));
+                st = nx;
+            }
+            TPL_STEP(read_frags(st, 1, f1), mma(f0));
+            mma(f1);
+            __builtin_amdgcn_sched_barrier(0);
+            return;
+        }
+    }
     __syncthreads();  // the LDS is free: the previous tile's reads are done
     issue(0, 0);
     wait_dma();
@@ -520,6 +582,9 @@ hipError_t launch_variant(const GemmParams &gp, int nxb, int nwb, hipStream_t st
         if (nxb == 2)
             return nwb == 3 ? launch_tm<2, 3, OUT_BF16, HAS_BIAS, ACT>(gp, stream)
                             : launch_tm<2, 4, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+        if (nxb == 4)
+            return nwb == 3 ? launch_tm<4, 3, OUT_BF16, HAS_BIAS, ACT>(gp, stream)
+                            : launch_tm<4, 4, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
         if (nwb == 3) {
             switch (nxb) {
             case 6: return launch_tm<6, 3, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
@@ -547,11 +612,13 @@ hipError_t launch_variant(const GemmParams &gp, int nxb, int nwb, hipStream_t st
 // 256 CUs: 4608 x 2304 x 6144 takes 252 tiles of 224 x 192 (one round) instead of 216 of
 // 192 x 256 (119.8 -> 112.2 us in the bench step), 4608 x 4608 x 6144 504 of them (231.7 ->
 // 225.7 us), 4608 x 9216 x 6144 756 of 224 x 256, rowwise 4608 x 6144 x 2304 432 of 256 x 256.
-// 64-row tiles (plain epilogues only) serve a few hundred rows, where the larger tiles leave
-// CUs idle; each of their tiles streams a whole weight panel for 64 rows, so they cost
-// about 2.7 (x 256) and 3.1 (x 192) times a 256 x 256 tile per flop (fitted to back-to-back
-// runs: 256 x 9216 x 6144 took 87 us in 192 tiles of 64 x 192 against 99 us in 96 of
-// 192 x 192; 512 x 3072 x 3072 30 against 39 us).
+// 64- and 128-row tiles (plain epilogues only) serve a few hundred rows, where the larger
+// tiles leave CUs idle.  Their factors, 1.30 (128 x 256), 1.45 (128 x 192), 1.97 (64 x 256)
+// and 2.2 (64 x 192), are fitted to back-to-back runs of every tile shape on 256 to 1536 rows
+// of a 9216 x 6144 weight and three smaller products, where the choice then matched the
+// fastest shape on every one: 256 rows take 64 x 192 tiles (61.7 us against 99.6 in
+// 192 x 192), 512 rows 128 x 192 (74.0 against 104.9), 768 rows 128 x 256 (88.6 against
+// 112.3), 1024 rows 224 x 192 as before.
 struct TileChoice {
     int nxb, nwb;
 };
@@ -562,12 +629,13 @@ TileChoice pick_tile(int M, int N, int K, bool gated, int cus)
         int nxb, nwb;
         double per_flop;
     };
-    static const Cand kCands[8] = {{8, 4, 1.0},  {7, 4, 1.025}, {6, 4, 1.05}, {8, 3, 1.08},
-                                   {7, 3, 1.12}, {6, 3, 1.27},  {2, 4, 2.7},  {2, 3, 3.1}};
+    static const Cand kCands[10] = {{8, 4, 1.0},  {7, 4, 1.025}, {6, 4, 1.05}, {8, 3, 1.08},
+                                    {7, 3, 1.12}, {6, 3, 1.27},  {4, 4, 1.30}, {4, 3, 1.45},
+                                    {2, 4, 1.97}, {2, 3, 2.2}};
     TileChoice best{8, 4};
     double best_cost = -1;
     for (const Cand &cd : kCands) {
-        if ((gated && (cd.nwb != 4 || cd.nxb == 2)) || (cd.nxb == 7 && K < 3072))
+        if ((gated && (cd.nwb != 4 || cd.nxb < 6)) || (cd.nxb == 7 && K < 3072))
             continue;
         const int bm = 32 * cd.nxb;
         const int cols = cd.nwb == 4 ? (gated ? 128 : 256) : 192;

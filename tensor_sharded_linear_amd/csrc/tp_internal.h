@@ -34,7 +34,7 @@ int cu_count();
 
 // Tiled MFMA GEMM (M > kNarrowMaxM).  Requires K % 64 == 0, N % 16 == 0.
 hipError_t launch_gemm(const LinearProblem &p, hipStream_t stream);
-// Output tile launch_gemm picks for p on the current device: rows 256, 224, 192 or 64,
+// Output tile launch_gemm picks for p on the current device: rows 256, 224, 192, 128 or 64,
 // columns 256 or 192 (128 outputs with SwiGLU).
 void gemm_tile_shape(const LinearProblem &p, int *rows, int *cols);
 

@@ -303,9 +303,10 @@ def test_tile_shape_query():
     assert q(64, 512, 256, "gelu_tanh") == (64, 4)        # the tiny MLP's colwise GEMM
     assert q(33, 2080, 128, "swiglu") == (48, 12)
     assert q(65, 9216, 6144) == (96, 36) and q(128, 9216, 6144) == (128, 36)
-    assert q(129, 9216, 6144) == (64, 192)                # past 128 rows: tiled kernel, 64-row
-    assert q(384, 9216, 6144) == (64, 256)                # tiles while they fill the CUs better
-    assert q(512, 9216, 6144) == (192, 192)
+    assert q(129, 9216, 6144) == (64, 192)                # past 128 rows: tiled kernel, 64- and
+    assert q(384, 9216, 6144) == (64, 256)                # 128-row tiles while they fill the CUs
+    assert q(512, 9216, 6144) == (128, 192)               # better
+    assert q(768, 9216, 6144) == (128, 256) and q(1024, 9216, 6144) == (224, 192)
     assert q(300, 3072, 128, "swiglu") == (192, 128)      # no 64-row SwiGLU tile
     assert q(4608, 2304, 6144) == (224, 192)              # 252 tiles, one round
     assert q(4608, 4608, 6144, "gelu_tanh") == (224, 192)  # 504 tiles, 1.97 rounds

@@ -3,8 +3,8 @@ kernel for up to 128 rows and the skinny weight-streaming kernel) against the
 oracle, through the C ABI.
 
 Ragged shapes span several tiles with partial tiles on both edges.  The
-kernel picks its tile shape per problem (64, 192, 224 or 256 rows by 192 or
-256 columns, whichever needs the least time in rounds of tiles over the CUs;
+kernel picks its tile shape per problem (64, 128, 192, 224 or 256 rows by 192
+or 256 columns, whichever needs the least time in rounds of tiles over the CUs;
 224 rows only for K >= 3072; tp_linear_tile_shape reports the choice).  On a
 256-CU device the RAGGED shapes with more than 128 rows and the first LARGE one
 run 64 x 192 tiles, the second LARGE one 224 x 192; the RAGGED shapes with 16

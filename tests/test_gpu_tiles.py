@@ -1,7 +1,8 @@
 """Every tile shape of the tiled GEMM with every epilogue, through the C ABI.
 
 The tiled kernel has one instance per tile shape (192, 224 or 256 rows by 192
-or 256 columns, and 64 rows by 192 or 256 columns for the plain epilogues;
+or 256 columns, and 64 or 128 rows by 192 or 256 columns for the plain
+epilogues;
 SwiGLU always 256 weight rows = 128 outputs), output dtype,
 bias or not, and epilogue.  For each shape the library can choose, a problem
 that gets it is found with tp_linear_tile_shape (on the device that runs the
@@ -27,7 +28,7 @@ from helpers import abs_dot, bits_to_dev, check_close, check_swiglu, dev_to_f64,
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(r, c) for r in (256, 224, 192, 64) for c in (256, 192)]
+SHAPES = [(r, c) for r in (256, 224, 192, 128, 64) for c in (256, 192)]
 SUB_ROWS = 160
 
 
@@ -87,3 +88,31 @@ def test_every_swiglu_tile_height(rows):
         check_swiglu(dev_to_f64(y[idx]), x, w, b if bias else None, out == torch.bfloat16, rows=srows, what=what)
         y_sub = tsl.tp_linear_colwise(xd[:SUB_ROWS], wd, bd if bias else None, act="swiglu", out_dtype=out)
         assert torch.equal(y[:SUB_ROWS], y_sub), what + ": differs from the same rows computed alone"
+
+
+# The 64- and 128-row tiles keep several k-tiles in flight (4 stages for 64 x 192, 3 for the
+# others) when K has at least that many k-tiles, and double buffer below that.  These
+# problems run each of them at 3, 4, 5 and 25 k-tiles: the double-buffered path, exactly the
+# stage count (every load issued before the loop), one more, and a long loop whose last
+# iterations wait for everything.
+MULTISTAGE = [((64, 192), 136, 1024), ((64, 256), 328, 8192), ((128, 192), 648, 6144), ((128, 256), 648, 8192)]
+
+
+@pytest.mark.parametrize("tile,M,N", MULTISTAGE)
+@pytest.mark.parametrize("K", [192, 256, 320, 1600])
+def test_multistage_tiles_integer_exact(tile, M, N, K):
+    if tsl.tp_linear_tile_shape(M, N, K) != tile:
+        pytest.skip(f"{M}x{N}x{K} takes another tile on this device's CU count")
+    rng = np.random.default_rng(tile[0] + tile[1] + K)
+    x = si.int_bf16(rng, (M, K), -3, 3)
+    w = si.int_bf16(rng, (N, K), -3, 3)
+    b = si.int_bf16(rng, (N,), -8, 8)
+    xd, wd, bd = bits_to_dev(x), bits_to_dev(w), bits_to_dev(b)
+    y = tsl.tp_linear_colwise(xd, wd, bd, out_dtype=torch.float32)
+    srows = sample_rows(M, 8, seed=K, tile=tile[0])
+    idx = torch.from_numpy(srows).cuda()
+    assert np.array_equal(dev_to_f64(y[idx]), oracle.colwise(x, w, b, rows=srows))
+    y_sub = tsl.tp_linear_colwise(xd[:SUB_ROWS], wd, bd, out_dtype=torch.float32)
+    assert torch.equal(y[:SUB_ROWS], y_sub)
+    p = tsl.tp_linear_rowwise(xd, wd)
+    assert np.array_equal(dev_to_f64(p[idx]), oracle.colwise(x, w, rows=srows))
