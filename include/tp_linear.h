@@ -142,10 +142,10 @@ tp_status tp_linear_rowwise(const void *x_shard, int64_t ldx, const void *w_shar
  * outputs, not the 2 N weight rows) on the current device: *tile_rows and
  * *tile_cols receive the tiled kernel's output tile (rows 256, 224, 192, 128 or 64;
  * columns 256 or 192, or 128 outputs with SwiGLU); for the split-K kernel
- * (up to 128 rows) 16 ceil(M / 16) rows (a multiple of 16, 96 for 65-96
- * rows, 128 above) and the run of 4 to 48 output columns (at most 16 with
- * SwiGLU) that each workgroup owns; or
- * both 0 when the weight-streaming kernel would run.  The choice depends on the shape and on
+ * (up to 128 rows) the rows its instance holds (16, 32, 48, 64, 96 or 128,
+ * the smallest that covers M) and the run of 4 to 48 output columns (at most
+ * 16 with SwiGLU) that each workgroup owns; or both 0 when the
+ * weight-streaming kernel would run.  The choice depends on the shape and on
  * the device's compute-unit count.  It lets a caller check results at the
  * tiles' real edges.  No device work, no allocation.
  * Errors: TP_ERR_INVALID_ARG for a null output pointer, an unknown act, or

@@ -101,7 +101,7 @@ tp_status run_linear(const char *fn, const tpl::LinearProblem &p, hipStream_t st
     hipError_t e;
     if (!p.swiglu && tpl::gemv_supports(p.M, p.K))
         e = tpl::launch_gemv(p, stream);
-    else if (tpl::narrow_supports(p.M))
+    else if (tpl::narrow_supports(p))
         e = tpl::launch_narrow(p, stream);
     else
         e = tpl::launch_gemm(p, stream);
@@ -201,7 +201,7 @@ tp_status tp_linear_tile_shape(int64_t M, int64_t N, int64_t K, tp_act act, int6
         return TP_OK;
     }
     int rows = 0, cols = 0;
-    if (tpl::narrow_supports(M))
+    if (tpl::narrow_supports(p))
         tpl::narrow_tile_shape(p, &rows, &cols);
     else
         tpl::gemm_tile_shape(p, &rows, &cols);

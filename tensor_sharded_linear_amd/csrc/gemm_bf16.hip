@@ -640,6 +640,8 @@ TileChoice pick_tile(int M, int N, int K, bool gated, int cus)
         const int bm = 32 * cd.nxb;
         const int cols = cd.nwb == 4 ? (gated ? 128 : 256) : 192;
         const int64_t tiles = (int64_t)((M + bm - 1) / bm) * ((N + cols - 1) / cols);
+        if (tiles > ((int64_t)1 << 22))
+            continue;  // the launch's thread count must stay below 2^32 (256 x 256 always fits)
         const double cost = (double)((tiles + cus - 1) / cus) * bm * (64 * cd.nwb) * cd.per_flop;
         if (best_cost < 0 || cost < best_cost) {
             best = TileChoice{cd.nxb, cd.nwb};

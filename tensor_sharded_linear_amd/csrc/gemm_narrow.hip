@@ -375,7 +375,14 @@ int pick_rows(int64_t M, int64_t N, bool gated, int cus)
 
 }  // namespace
 
-bool narrow_supports(int64_t M) { return M >= 1 && M <= kNarrowMaxM; }
+bool narrow_supports(const LinearProblem &pr)
+{
+    if (pr.M < 1 || pr.M > kNarrowMaxM)
+        return false;
+    // One 256-thread workgroup per run: the launch's thread count must stay below 2^32.
+    const int rows = pick_rows(pr.M, pr.N, pr.swiglu, cu_count());
+    return (pr.N + rows - 1) / rows <= ((int64_t)1 << 23);
+}
 
 void narrow_tile_shape(const LinearProblem &pr, int *rows, int *cols)
 {
@@ -386,7 +393,7 @@ void narrow_tile_shape(const LinearProblem &pr, int *rows, int *cols)
 
 hipError_t launch_narrow(const LinearProblem &pr, hipStream_t stream)
 {
-    if (!narrow_supports(pr.M))
+    if (!narrow_supports(pr))
         return hipErrorInvalidValue;  // the caller checks narrow_supports()
     NarrowParams np;
     np.x = pr.x;

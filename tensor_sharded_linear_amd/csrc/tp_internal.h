@@ -53,7 +53,7 @@ hipError_t launch_gemv(const LinearProblem &p, hipStream_t stream);
 // kernel does not take: all M rows and 32 output columns (16 with SwiGLU) per
 // workgroup, K split across its waves.  Same requirements as the tiled kernel.
 constexpr int64_t kNarrowMaxM = 128;
-bool narrow_supports(int64_t M);
+bool narrow_supports(const LinearProblem &p);
 void narrow_tile_shape(const LinearProblem &p, int *rows, int *cols);
 hipError_t launch_narrow(const LinearProblem &p, hipStream_t stream);
 

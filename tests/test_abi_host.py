@@ -307,6 +307,10 @@ def test_tile_shape_query():
     assert q(384, 9216, 6144) == (64, 256)                # 128-row tiles while they fill the CUs
     assert q(512, 9216, 6144) == (128, 192)               # better
     assert q(768, 9216, 6144) == (128, 256) and q(1024, 9216, 6144) == (224, 192)
+    # launch sizes: a split-K launch has at most 2^23 workgroups of 256 threads, a tiled one at
+    # most 2^22 tiles of 512 threads; past that the next kernel that fits takes the problem
+    assert q(8, 48 << 23, 64) == (16, 48)
+    assert q(8, (48 << 23) + 48, 64) == (64, 256) and q(8, 1 << 30, 64) == (64, 256)
     assert q(300, 3072, 128, "swiglu") == (192, 128)      # no 64-row SwiGLU tile
     assert q(4608, 2304, 6144) == (224, 192)              # 252 tiles, one round
     assert q(4608, 4608, 6144, "gelu_tanh") == (224, 192)  # 504 tiles, 1.97 rounds
