@@ -47,7 +47,7 @@ def _narrow(M, N, K, act="none"):
 RUNS = [(2080, 12), (4160, 20), (4112, 20), (8208, 36), (8224, 36)]
 
 
-@pytest.mark.parametrize("M", [9, 40, 64, 100, 128])
+@pytest.mark.parametrize("M", [9, 40, 64, 80, 100, 128])
 @pytest.mark.parametrize("N,run", RUNS)
 def test_narrow_balanced_runs_integer_exact(M, N, run):
     rng = np.random.default_rng(1500 + M + N)
