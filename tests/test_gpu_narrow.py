@@ -232,3 +232,20 @@ def test_narrow_repeat_runs_are_bitwise_identical():
     y0 = tsl.tp_linear_rowwise(x, w)
     for _ in range(3):
         assert torch.equal(tsl.tp_linear_rowwise(x, w), y0)
+
+
+@pytest.mark.parametrize("M", [5, 6, 128, 129])
+def test_kernel_boundaries_integer_exact(M):
+    """Both sides of each boundary between the three GEMM kernels: 5 rows take the
+    weight-streaming kernel and 6 the split-K kernel (K = 1024), 128 rows the split-K kernel
+    and 129 the tiled one; integer inputs with bias and GELU-free fp32 output: exact."""
+    rng = np.random.default_rng(8000 + M)
+    N, K = 2064, 1024
+    x = si.int_bf16(rng, (M, K), -3, 3)
+    w = si.int_bf16(rng, (N, K), -3, 3)
+    b = si.int_bf16(rng, (N,), -8, 8)
+    rows, cols = tsl.tp_linear_tile_shape(M, N, K)
+    kernel = "weight-streaming" if (rows, cols) == (0, 0) else ("split-K" if cols <= 48 else "tiled")
+    assert kernel == {5: "weight-streaming", 6: "split-K", 128: "split-K", 129: "tiled"}[M]
+    y = tsl.tp_linear_colwise(bits_to_dev(x), bits_to_dev(w), bits_to_dev(b), out_dtype=torch.float32)
+    assert np.array_equal(dev_to_f64(y), oracle.colwise(x, w, b))
