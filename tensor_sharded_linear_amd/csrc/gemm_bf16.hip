@@ -9,8 +9,10 @@
 // block of W and X with an fp32 store and no bias (the partial sum).
 //
 // Design for gfx950:
-//  * 256 x 256 output tile per workgroup, or 224 / 192 rows and 192 columns
-//    where that fills the CUs better (pick_tile), K step 64, 512 threads = 8
+//  * BM x BN output tile per workgroup: 256, 224 or 192 rows by 256 or 192
+//    columns for many rows, 128 or 64 rows for a few hundred, whichever fills
+//    the CUs best (pick_tile); up to 128 rows the split-K kernel
+//    (gemm_narrow.hip) runs instead.  K step 64, 512 threads = 8
 //    waves in a 2 (M) x 4 (N) grid; each wave owns a (BM/2) x (BN/4) sub-tile
 //    held as NXB x NWB MFMA 16x16 fp32 accumulators (at most 128 accumulator
 //    registers per lane).  Two waves per SIMD, so one wave's LDS fragment reads
@@ -27,7 +29,9 @@
 //    workload shape.
 //  * Operands go HBM/L2 -> LDS by direct-to-LDS DMA (global_load_lds_dwordx4),
 //    no VGPR staging, double-buffered: 2 stages x (X tile + W tile), at most
-//    128 KiB of the 160 KiB LDS.
+//    128 KiB of the 160 KiB LDS.  The 64- and 128-row tiles, whose MFMA work per
+//    k-tile is too short to cover the next k-tile's loads, keep 3 or 4 stages
+//    (at most 144 KiB) and 2 or 3 k-tiles in flight (mainloop).
 //  * Fragments are double-buffered in registers at k32 granularity: while
 //    the NXB x NWB MFMAs of one k32 step run, the NXB + NWB fragments of the
 //    next step are read from LDS, one read after each of the first MFMAs.  The single
@@ -68,9 +72,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define TPL_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
-// The tile shape is two template parameters, the 16-row MFMA blocks per wave NXB = 8, 7
-// or 6 (256, 224 or 192 rows) and the 16-column blocks per wave NWB = 4 or 3 (256 or
-// 192 columns); pick_tile chooses the one that fills the CUs best for the shape.
+// The tile shape is two template parameters, the 16-row MFMA blocks per wave NXB = 8, 7,
+// 6, 4 or 2 (256, 224, 192, 128 or 64 rows) and the 16-column blocks per wave NWB = 4 or 3
+// (256 or 192 columns); pick_tile chooses the one that fills the CUs best for the shape.
 constexpr int BK = 64;
 constexpr int kThreads = 512;     // 8 waves in a 2 (M) x 4 (N) grid
 constexpr int kWavesN = 4;

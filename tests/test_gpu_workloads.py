@@ -5,7 +5,7 @@ Index work (slices, QKV split, CONCAT) and the SUM combine are checked bit for
 bit on whole tensors.  GEMM outputs are checked against the oracle on sampled
 rows, all columns, every rank: rows 0, 1 and M - 1, both rows at every edge of
 the output tiles that the library picks for that GEMM's shape (192, 224 or 256
-rows, from tp_linear_tile_shape), and seeded random rows.  Whole tensors are
+rows at these sizes, from tp_linear_tile_shape), and seeded random rows.  Whole tensors are
 checked through GPU-side invariants of the method: the colwise shards' outputs
 gather bit for bit to the unsharded output (the tiled kernel has no split-K, so
 each output element sees the same products in the same order whatever the tile
