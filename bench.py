@@ -89,12 +89,16 @@ def parse():
                     help="instead of the step: every GEMM shape of the step through this library and through "
                          "torch.matmul / torch.mm (hipBLASLt), plain products without epilogue, back to back on "
                          "three rotating operand sets; writes a markdown table to OUT_MD")
+    ap.add_argument("--vendor-square", metavar="OUT_MD",
+                    help="instead of the step: large products whose 256 x 256 tiles fill the CUs in whole "
+                         "rounds (8192 and 16384 rows and columns) through this library and through "
+                         "torch.matmul (hipBLASLt), measured like --vendor; writes a markdown table to OUT_MD")
     ap.add_argument("--configs-trace", metavar="TRACE_CSV",
                     help="no GPU: from the rocprofv3 kernel trace of a --configs run, print per-kernel medians "
                          "of the dispatches right after the cache-flush read (cold) and of the others (warm)")
     ap.add_argument("--pmc-summary", nargs="+", metavar="RUN_DIR",
                     help="no GPU: average every counter of rocprofv3 --pmc runs per kernel of this library "
-                         "(name and grid) and print a markdown table")
+                         "and per hipBLASLt GEMM kernel (name and grid) and print a markdown table")
     return ap.parse_args()
 
 
@@ -636,6 +640,9 @@ def main():
         return
     if args.vendor:
         vendor_bench(args)
+        return
+    if args.vendor_square:
+        vendor_bench(args, square=True)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -1313,6 +1320,10 @@ FAMILY_KERNEL = {"slice": "copy_segments_kernel", "concat": "copy_segments_kerne
 VENDOR_SHAPES = [("colwise", 4608, 2304, 6144), ("colwise", 4608, 4608, 6144), ("colwise", 4608, 9216, 6144),
                  ("rowwise", 4608, 6144, 768), ("rowwise", 4608, 6144, 1536), ("rowwise", 4608, 6144, 2304),
                  ("rowwise", 4608, 6144, 3072), ("rowwise", 4608, 6144, 4608), ("rowwise", 4608, 6144, 9216)]
+# Large products whose 256 x 256 tiles fill the CUs in whole rounds (4 and 16 rounds), and the
+# step's largest product for comparison.
+SQUARE_SHAPES = [("colwise", 8192, 8192, 4096), ("colwise", 8192, 8192, 8192), ("colwise", 16384, 16384, 8192),
+                 ("colwise", 4608, 9216, 6144)]
 # Few token rows: the adaLN shard's weight (9216 x 6144) and the tp 4 rowwise_split_input
 # shard (36864 x 1536) at 1-64 rows, the tiny MLP's two GEMMs, and 128-512 rows (tiled kernel).
 FEW_ROW_SHAPES = ([("colwise", m, 9216, 6144) for m in (1, 4, 6, 16, 32, 64, 128, 256, 512)]
@@ -1320,19 +1331,20 @@ FEW_ROW_SHAPES = ([("colwise", m, 9216, 6144) for m in (1, 4, 6, 16, 32, 64, 128
                      ("colwise", 64, 512, 256), ("rowwise", 64, 256, 512)])
 
 
-def vendor_bench(args):
+def vendor_bench(args, square=False):
     """The step's GEMM shapes (no bias or activation) through this library and through the
     vendor BLAS that torch calls (hipBLASLt): colwise with bf16 output (torch.matmul), rowwise
     with fp32 output (torch.mm with out_dtype).  Each measurement is 3 warm-up calls, then 20
     calls back to back on three rotating operand sets under one event pair (dispatch gaps
     included, as in the step); the two implementations alternate twice per shape and the
-    faster of each pair of measurements is kept."""
+    faster of each pair of measurements is kept.  With square=True the shapes are the large
+    products of SQUARE_SHAPES instead (10 calls per measurement)."""
     import torch
     import tensor_sharded_linear_amd as tsl
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tsl.load_library()
-    reps, warm = 20, 3
+    reps, warm = (10, 2) if square else (20, 3)
     stream = torch.cuda.current_stream()
 
     def timed(fn):
@@ -1355,7 +1367,10 @@ def vendor_bench(args):
         return us
 
     rows = []
-    shapes = [(s, "step") for s in VENDOR_SHAPES] + [(s, "few") for s in FEW_ROW_SHAPES]
+    if square:
+        shapes = [(s, "square") for s in SQUARE_SHAPES]
+    else:
+        shapes = [(s, "step") for s in VENDOR_SHAPES] + [(s, "few") for s in FEW_ROW_SHAPES]
     for (kind, M, N, K), group in shapes:
         g = torch.Generator(device=dev)
         g.manual_seed(M * 7 + N * 3 + K)
@@ -1387,6 +1402,9 @@ def vendor_bench(args):
                          tile=tsl.tp_linear_tile_shape(M, N, K)))
         print(f"# {kind} {M}x{N}x{K}: ours {a:.1f} us, vendor {b:.1f} us", file=sys.stderr, flush=True)
         del xs, ws
+    if square:
+        vendor_square_md(args.vendor_square, rows)
+        return
     md = ["# GEMM shapes: this library against the vendor BLAS (hipBLASLt)", "",
           "Command (run from the repository root on one MI355X):", "", "```",
           "python3 bench.py " + " ".join(sys.argv[1:]), "```", "",
@@ -1427,6 +1445,32 @@ def vendor_bench(args):
     with open(args.vendor, "w") as f:
         f.write("\n".join(md) + "\n")
     print(json.dumps({"vendor_comparison": rows}), flush=True)
+
+
+def vendor_square_md(path, rows):
+    """The --vendor-square table."""
+    md = ["# Large products: this library against the vendor BLAS (hipBLASLt)", "",
+          "Command (run from the repository root on one MI355X):", "", "```",
+          "python3 bench.py " + " ".join(sys.argv[1:]), "```", "",
+          "Plain colwise products (bf16 output, no bias or activation) of random normal bf16 operands "
+          "whose 256 x 256 output tiles cover the 256 CUs in whole rounds, beside the step's largest "
+          "product.  Measured as in `gemm_vs_vendor_blas.md` (three rotating operand sets, a spin kernel, "
+          "then 10 calls back to back under one event pair; the two implementations alternate twice and "
+          "the faster measurement of each is kept).  Percent of the 2.5 PFLOP/s bf16 dense peak.", "",
+          "| M x N x K | tiles of this library | rounds over 256 CUs | this library µs | TFLOP/s | % | "
+          "hipBLASLt µs | TFLOP/s | % | vendor / library time |",
+          "|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        m, n, _ = (int(v) for v in r["shape"].split("x"))
+        t0, t1 = r["tile"]
+        tiles = -(-m // t0) * -(-n // t1)
+        md.append(f"| {r['shape']} | {t0}x{t1} ({tiles}) | {tiles / 256:.2f} | {r['ours_us']} | "
+                  f"{r['ours_tflops']:.0f} | {100 * r['ours_tflops'] / PEAK_BF16_TFLOPS:.1f} | {r['vendor_us']} | "
+                  f"{r['vendor_tflops']:.0f} | {100 * r['vendor_tflops'] / PEAK_BF16_TFLOPS:.1f} | "
+                  f"{r['vendor_us'] / r['ours_us']:.3f} |")
+    with open(path, "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(json.dumps({"vendor_square": rows}), flush=True)
 
 
 def cold_trace(trace_csv, cold_md):
@@ -1480,38 +1524,70 @@ def cold_trace(trace_csv, cold_md):
     print("\n".join(out))
 
 
+def _short_kernel(name):
+    """A short label for a kernel of this library or a hipBLASLt GEMM kernel; None for others."""
+    short = name.replace("void ", "").replace("tpl::(anonymous namespace)::", "").split("(")[0]
+    if short.startswith(("gemm_", "gemv_", "copy_", "combine_")):
+        return short
+    if "Cijk" in name:
+        mt = next((t for t in name.split("_") if t.startswith("MT")), "MT?")
+        return f"hipBLASLt {mt}" + (" stream-K" if "_SK" in name else "")
+    return None
+
+
 def pmc_summary(dirs):
-    """Per kernel of this library (short name and grid size), the mean of every counter over its
-    dispatches, across one or more rocprofv3 --pmc run directories (one counter set each)."""
+    """Per kernel of this library, and per hipBLASLt GEMM kernel (short name and grid size), the
+    mean of every counter over its dispatches, across one or more rocprofv3 --pmc run directories
+    (one counter set each), with the mean dispatch time under counter collection.  Where a run
+    collected GRBM_GUI_ACTIVE (summed over the 8 XCDs), the clock (GUI-active cycles per XCD over
+    the dispatch time) is added, and the busy fractions MfmaUtil (as rocprofv3 derives it),
+    TD_TD_BUSY and TA_TA_BUSY per CU cycle, where collected."""
     import csv
     import glob
 
-    acc = {}   # (kernel, grid) -> counter -> [values]
-    for d in dirs:
-        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            per = {}
-            with open(path) as f:
-                for r in csv.DictReader(f):
-                    short = r["Kernel_Name"].replace("void ", "").replace("tpl::(anonymous namespace)::", "")
-                    short = short.split("(")[0]
-                    if not short.startswith(("gemm_", "gemv_", "copy_", "combine_")):
-                        continue
-                    key = (short, int(r["Grid_Size"]), int(r["Dispatch_Id"]))
-                    per.setdefault(key, {})
-                    per[key][r["Counter_Name"]] = per[key].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-            for (k, grid, _), cnt in per.items():
-                e = acc.setdefault((k, grid), {})
-                for c, v in cnt.items():
-                    e.setdefault(c, []).append(v)
+    paths = [p for d in dirs for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)]
+    # Runs of one program dispatch the same kernels in the same order, so a run that counted
+    # MfmaFlopsBF16 labels every run's dispatch of a GEMM with its flops (its shape).
+    gflop = {}
+    for path in paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == "MfmaFlopsBF16" and _short_kernel(r["Kernel_Name"]):
+                    gflop[int(r["Dispatch_Id"])] = round(float(r["Counter_Value"]) / 1e9, 1)
+    acc = {}   # (kernel, grid, GFLOP) -> counter -> [values]
+    for path in paths:
+        per = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                short = _short_kernel(r["Kernel_Name"])
+                if short is None:
+                    continue
+                key = (short, int(r["Grid_Size"]), int(r["Dispatch_Id"]))
+                e = per.setdefault(key, {})
+                e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                e["us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        for (k, grid, disp), cnt in per.items():
+            e = acc.setdefault((k, grid, gflop.get(disp, "-")), {})
+            if "GRBM_GUI_ACTIVE" in cnt:
+                gui = cnt["GRBM_GUI_ACTIVE"] / N_XCC
+                e.setdefault("clock GHz", []).append(gui / cnt["us"] / 1e3)
+                for c in ("TD_TD_BUSY", "TA_TA_BUSY"):
+                    if c in cnt:
+                        e.setdefault(c + " / CU cycle", []).append(cnt[c] / (gui * 256))
+            for c, v in cnt.items():
+                e.setdefault(c, []).append(v)
     if not acc:
-        raise SystemExit("no counter_collection.csv with this library's kernels under " + " ".join(dirs))
+        raise SystemExit("no counter_collection.csv with these kernels under " + " ".join(dirs))
     names = sorted({c for e in acc.values() for c in e})
-    print("| kernel | grid (threads) | dispatches | " + " | ".join(names) + " |")
-    print("|---|---|---|" + "---|" * len(names))
-    for (k, grid), e in sorted(acc.items()):
-        n = max(len(v) for v in e.values())
-        vals = [f"{sum(e[c]) / len(e[c]):.0f}" if c in e else "-" for c in names]
-        print(f"| `{k}` | {grid} | {n} | " + " | ".join(vals) + " |")
+
+    def fmt(v):
+        return f"{v:.0f}" if abs(v) >= 100 else f"{v:.3g}"
+    print("| kernel | grid (threads) | GFLOP | dispatches | " + " | ".join(names) + " |")
+    print("|---|---|---|---|" + "---|" * len(names))
+    for (k, grid, gf), e in sorted(acc.items(), key=lambda kv: (kv[0][0], kv[0][1], str(kv[0][2]))):
+        n = min(len(v) for v in e.values())  # a counter of one run: the dispatches per run
+        vals = [fmt(sum(e[c]) / len(e[c])) if c in e else "-" for c in names]
+        print(f"| `{k}` | {grid} | {gf} | {n} | " + " | ".join(vals) + " |")
 
 
 def configs_trace(path):

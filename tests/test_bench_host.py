@@ -119,3 +119,42 @@ def test_counters_scale_bytes_by_the_calibration_copy(tmp_path, monkeypatch):
     assert t["ratio_to_algorithmic"] == pytest.approx(2.56)
     md = open(tmp_path / "profiles" / "dit_block_step_counters.md").read()
     assert "| slice: w1 P2 | 1 | 0.0 | 0.0 | 0.0 | 1.024 |" in md
+
+
+def _pmc_run(path, rows):
+    """rows: (dispatch id, kernel name, counter, value, duration ns)."""
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value",
+                    "Start_Timestamp", "End_Timestamp"])
+        for disp, name, counter, value, ns in rows:
+            w.writerow([disp, 1024, name, counter, value, 1000, 1000 + ns])
+
+
+def test_pmc_summary_labels_dispatches_by_their_flops(tmp_path, capsys):
+    """Two runs of one program: the flops counted in the first label the same dispatch ids in
+    the second, so two shapes of one kernel and grid get separate rows; hipBLASLt kernels get a
+    short label and other kernels are left out."""
+    ours = "void tpl::(anonymous namespace)::gemm_bf16_nt_kernel<8, 4, true, false, 0>(tpl::GemmParams)"
+    vend = "Cijk_Alik_Bljk_BBS_BH_Bias_HA_S_SAV_UserArgs_MT256x256x64_MI16x16x1_SK3_gfx950"
+    other = "void at::native::elementwise_kernel<128, 4>(...)"
+    _pmc_run(tmp_path / "a", [(1, ours, "MfmaFlopsBF16", 2e9, 1000), (1, ours, "GRBM_GUI_ACTIVE", 8 * 2000, 1000),
+                              (2, ours, "MfmaFlopsBF16", 4e9, 2000), (2, ours, "GRBM_GUI_ACTIVE", 8 * 4000, 2000),
+                              (3, vend, "MfmaFlopsBF16", 2e9, 800), (3, vend, "GRBM_GUI_ACTIVE", 8 * 1600, 800),
+                              (4, other, "MfmaFlopsBF16", 0, 10)])
+    _pmc_run(tmp_path / "b", [(1, ours, "SQ_WAIT_ANY", 10, 1000), (2, ours, "SQ_WAIT_ANY", 30, 2000),
+                              (3, vend, "SQ_WAIT_ANY", 5, 800)])
+    bench.pmc_summary([str(tmp_path / "a"), str(tmp_path / "b")])
+    out = capsys.readouterr().out.splitlines()
+    hdr = [h.strip() for h in out[0].strip("|").split("|")]
+    rows = [dict(zip(hdr, [c.strip() for c in line.strip("|").split("|")])) for line in out[2:]]
+    assert len(rows) == 3
+    by = {(r["kernel"], r["GFLOP"]): r for r in rows}
+    a = by[("`gemm_bf16_nt_kernel<8, 4, true, false, 0>`", "2.0")]
+    b = by[("`gemm_bf16_nt_kernel<8, 4, true, false, 0>`", "4.0")]
+    v = by[("`hipBLASLt MT256x256x64 stream-K`", "2.0")]
+    assert a["SQ_WAIT_ANY"] == "10" and b["SQ_WAIT_ANY"] == "30" and v["SQ_WAIT_ANY"] == "5"
+    # clock = GUI-active cycles per XCD over the dispatch time: 2000 cycles in 1 us = 2 GHz
+    assert a["clock GHz"] == "2" and b["clock GHz"] == "2" and v["clock GHz"] == "2"
+    assert a["dispatches"] == "1"
