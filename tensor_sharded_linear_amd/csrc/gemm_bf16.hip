@@ -21,12 +21,14 @@
 //    this kernel (MFMA-busy cycles over GUI-active cycles, and GUI-active
 //    cycles over time) show the MFMA pipe busy 64-66% of cycles with random,
 //    constant or all-zero operands alike, while the clock falls from 2.41 GHz
-//    (zeros) to 1.76 GHz (random) back to back; schedule changes that raise
-//    the busy fraction lower the clock by as much.  So energy per flop, and
-//    the fill of the CUs, set the speed.  Counting operand reads plus
-//    accumulator read and write, the 16x16x32 form moves 20% fewer register
-//    bytes per flop than 32x32x16, and it measured 3-9% faster on every
-//    workload shape.
+//    (zeros) to 1.76 GHz (random) back to back; changes to this schedule that
+//    raised the busy fraction lowered the clock by as much, so the fill of the
+//    CUs sets its speed.  (A vendor kernel of 4 waves, one per SIMD, keeps the
+//    pipe 79-85% busy under the same cap on products its 256 x 256 tiles fill
+//    in whole rounds; 4-wave versions of this kernel measured 1-12% slower.)
+//    Counting operand reads plus accumulator read and write, the 16x16x32
+//    form moves 20% fewer register bytes per flop than 32x32x16, and it
+//    measured 3-9% faster on every workload shape.
 //  * Operands go HBM/L2 -> LDS by direct-to-LDS DMA (global_load_lds_dwordx4),
 //    no VGPR staging, double-buffered: 2 stages x (X tile + W tile), at most
 //    128 KiB of the 160 KiB LDS.  The 64- and 128-row tiles, whose MFMA work per
