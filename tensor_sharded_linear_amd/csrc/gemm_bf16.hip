@@ -548,6 +548,200 @@ __device__ __forceinline__ void zero(f32x4 (&acc)[NXB][NWB])
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// ---- Four-wave tiles: the 192-, 224- and 256-row tiles of the plain, bias and GELU epilogues.
+//
+// 256 threads = 4 waves in a 2 x 2 grid, one wave per SIMD, each owning (16 NXB) x (16 NWB)
+// outputs (NWB = 8 or 6: 256- or 192-column tiles) as NXB x NWB MFMA accumulators, up to 256
+// registers, held in the accumulation registers: each MFMA is written out with its
+// accumulator tied to those registers ("+a"), so the compiler never moves an accumulator
+// between register files inside the loop (it did, hundreds of moves per k-tile, when it
+// chose the registers itself).  Per wave and k32 step the fragment reads fall to
+// NXB + NWB for NXB x NWB MFMAs (12 for 32 MFMAs with eight waves of 128 x 64, 16 for 64
+// here), so the LDS serves a third fewer reads per flop.
+//
+// With one wave per SIMD nothing hides an instruction the wave spends not issuing MFMAs,
+// so the order of each k32 step is written out (the MFMAs clobber memory, which pins every
+// load between them): MFMA q, then, if q is a multiple of RS, the next fragment read, and if
+// q is 1 more than a multiple of DS, the next load of the k-tile after next.  The reads and
+// loads are spread evenly over the step.  Issued in bursts after the first MFMAs instead,
+// the same kernel measured 3-9% slower than the eight-wave tiles; spread, and with the loads
+// in their scalar-base form (dma16_sbase), it measured 1-13% faster on every shape of the
+// DiT block (bit-identical outputs).  Pipeline, LDS layout, swizzle and epilogue are those of
+// the eight-wave kernel: 2 LDS stages, one barrier per k-tile before its second k32 step.
+constexpr int kThreads4 = 256;
+constexpr int kWaves4 = kThreads4 / 64;
+
+// One 16-byte direct-to-LDS load per lane in its scalar-base form: a wave-uniform base
+// address plus the lane's 32-bit byte offset, with the LDS address of the wave's 1 KiB
+// destination in M0 (lane l writes 16 l bytes after it).  The builtin forms a 64-bit lane
+// address with two VALU instructions per load, which the single wave of a SIMD issues
+// between its MFMAs.  The load writes no register; the caller waits for it with an explicit
+// vmcnt wait before the barrier that publishes its data.  No other code of the kernel uses
+// M0, so clobbering it here is safe.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_sbase(const char *base, uint32_t off, uint16_t *dst)
+{
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)dst;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(off), "s"(base)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// acc += X[m0 .. m0 + BM - 1, :] . W[n0 .. n0 + BN - 1, :]^T over all of K, four waves.
+// Rows past the end are clamped (computed and discarded).
+template <int NXB, int NWB>
+__device__ __forceinline__ void mainloop4(const GemmParams &p, uint16_t *lds, const Ctx &c, int m0, int n0,
+                                          f32x4 (&acc)[NXB][NWB])
+{
+    constexpr int WM = 16 * NXB, WN = 16 * NWB, BM = 2 * WM, BN = 2 * WN;
+    constexpr int kDmaX = BM / 32, kDmaW = BN / 32, kDma = kDmaX + kDmaW;  // per lane and k-tile
+    constexpr int kXElems = BM * BK, kStageElems = (BM + BN) * BK;
+    constexpr int kMfma = NXB * NWB, kReads = NXB + NWB;
+    constexpr int RS = kMfma / kReads, DS = kMfma / kDma;
+    static_assert(RS >= 1 && DS >= 1 && (kReads - 1) * RS < kMfma && 1 % DS + (kDma - 1) * DS < kMfma,
+                  "the reads and loads of a k32 step fit between its MFMAs");
+    // DMA: instruction j of wave w fills LDS chunks [(4 j + w) * 64, +64) of a 64-column tile:
+    // lane l lands at tile row 32 j + 8 w + l / 8, stored position l % 8, so it fetches logical
+    // chunk (l % 8) ^ ((row >> 1) & 7) = (l % 8) ^ ((4 (w & 1) + l / 16) & 7).
+    const int dma_row = c.wave * 8 + (c.lane >> 3);
+    const int dma_chunk = (c.lane & 7) ^ ((((c.wave & 1) << 2) + (c.lane >> 4)) & 7);
+    // Fragments: lane l reads row l % 16 of a 16-row block, chunk (4 s + l / 16) ^ swz.
+    const int xrow_off = (c.wave_m * WM + (c.lane & 15)) * BK;
+    const int wrow_off = (c.wave_n * WN + (c.lane & 15)) * BK;
+    const int swz = (c.lane >> 1) & 7;
+    const int kh = c.lane >> 4;
+    uint32_t xoff[kDmaX], woff[kDmaW];
+#pragma unroll
+    for (int j = 0; j < kDmaX; ++j) {
+        const int gm = min(m0 + 32 * j + dma_row, p.M - 1);
+        xoff[j] = (uint32_t)(((int64_t)gm * p.ldx + dma_chunk * 8) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < kDmaW; ++j) {
+        const int gn = min(n0 + 32 * j + dma_row, p.N - 1);
+        woff[j] = (uint32_t)(((int64_t)gn * p.ldw + dma_chunk * 8) * 2);
+    }
+    const char *xbase = reinterpret_cast<const char *>(p.x);
+    const char *wbase = reinterpret_cast<const char *>(p.w);
+    auto dma = [&](int d, int stage, int k0) {  // load d of k-tile k0 / 64 into `stage`
+        uint16_t *xs = lds + stage * kStageElems;
+        if (d < kDmaX)
+            dma16_sbase(xbase + k0 * 2, xoff[d], xs + (d * kWaves4 + c.wave) * 512);
+        else
+            dma16_sbase(wbase + k0 * 2, woff[d - kDmaX], xs + kXElems + ((d - kDmaX) * kWaves4 + c.wave) * 512);
+    };
+    // read r of a k32 step: the X fragments first, then the W fragments (the next step's
+    // first MFMAs use W block 0 with every X block)
+    auto read = [&](int r, int stage, int s, Frags<NXB, NWB> &f) {
+        const uint16_t *xs = lds + stage * kStageElems;
+        const int cpos = ((s * 4 + kh) ^ swz) * 8;
+        if (r < NXB)
+            f.x[r] = *reinterpret_cast<const bf16x8 *>(xs + xrow_off + r * 16 * BK + cpos);
+        else
+            f.w[r - NXB] = *reinterpret_cast<const bf16x8 *>(xs + kXElems + wrow_off + (r - NXB) * 16 * BK + cpos);
+    };
+    // One k32 step on `cur`; READS: the next step's fragments (stage rstage, k32 step rs) into
+    // `nxt`; DMA: the loads of the k-tile at dk0 into stage dstage.
+    auto step = [&](const Frags<NXB, NWB> &cur, Frags<NXB, NWB> &nxt, auto READS, auto DMA, int rstage, int rs,
+                    int dstage, int dk0) {
+#pragma unroll
+        for (int q = 0; q < kMfma; ++q) {
+            const int j = q / NXB, i = q % NXB;  // W block by W block
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                         : "+a"(acc[i][j])
+                         : "v"(cur.w[j]), "v"(cur.x[i])
+                         : "memory");
+            if constexpr (decltype(DMA)::value) {
+                if (q % DS == 1 % DS && q / DS < kDma)
+                    dma(q / DS, dstage, dk0);
+            }
+            if constexpr (decltype(READS)::value) {
+                if (q % RS == 0 && q / RS < kReads)
+                    read(q / RS, rstage, rs, nxt);
+            }
+        }
+    };
+    using Yes = std::true_type;
+    using No = std::false_type;
+    const int T = p.K / BK;
+    Frags<NXB, NWB> f0, f1;
+#pragma unroll
+    for (int d = 0; d < kDma; ++d)
+        dma(d, 0, 0);
+    wait_dma();
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kReads; ++r)
+        read(r, 0, 0, f0);
+    if (T > 1) {
+#pragma unroll
+        for (int d = 0; d < kDma; ++d)
+            dma(d, 1, BK);
+    }
+    // Stage t % 2 holds k-tile t.  Step 0 runs on f0 while the step-1 fragments are read; the
+    // barrier then finds k-tile t + 1 landed and stage t % 2 read by every wave, so step 1
+    // loads k-tile t + 2 into it while it reads the next k-tile's step-0 fragments.
+    int t = 0;
+    for (; t < T - 2; ++t) {
+        const int st = t & 1;
+        step(f0, f1, Yes{}, No{}, st, 1, 0, 0);
+        wait_dma();
+        __syncthreads();
+        step(f1, f0, Yes{}, Yes{}, st ^ 1, 0, st, (t + 2) * BK);
+    }
+    for (; t < T - 1; ++t) {
+        const int st = t & 1;
+        step(f0, f1, Yes{}, No{}, st, 1, 0, 0);
+        wait_dma();
+        __syncthreads();
+        step(f1, f0, Yes{}, No{}, st ^ 1, 0, 0, 0);
+    }
+    step(f0, f1, Yes{}, No{}, (T - 1) & 1, 1, 0, 0);
+    step(f1, f0, No{}, No{}, 0, 0, 0, 0);
+    // The last MFMAs' results must be written before they are read as ordinary values; the
+    // empty statements keep every read of an accumulator after the wait.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NXB; ++i)
+#pragma unroll
+        for (int j = 0; j < NWB; ++j)
+            asm volatile("" : "+a"(acc[i][j]));
+}
+
+// One (32 NXB) x (32 NWB) output tile per workgroup of four waves.
+template <int NXB, int NWB, bool OUT_BF16, bool HAS_BIAS, int ACT>
+__global__ __launch_bounds__(kThreads4) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm4_bf16_nt_kernel(GemmParams p)
+{
+    static_assert(ACT != kActSwiglu, "the gated epilogue runs on the eight-wave tiles");
+    static_assert(NXB >= 6 && NXB <= 8 && (NWB == 6 || NWB == 8), "192-256 rows by 192 or 256 columns");
+    constexpr int BM = 32 * NXB, BN = 32 * NWB;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * (BM + BN) * BK];
+    Ctx c;
+    c.lane = threadIdx.x & 63;
+    c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    c.wave_m = c.wave >> 1;
+    c.wave_n = c.wave & 1;
+    int tm, tn;
+    tile_of(xcd_contiguous(blockIdx.x, p.tiles_m * p.tiles_n), p, tm, tn);
+    f32x4 acc[NXB][NWB];
+    zero<NXB, NWB>(acc);
+    mainloop4<NXB, NWB>(p, lds, c, tm * BM, tn * BN, acc);
+    epilogue<NXB, NWB, OUT_BF16, HAS_BIAS, ACT>(p, lds, c, tm * BM, tn * BN, acc);
+}
+
+template <int NXB, int NWB, bool OUT_BF16, bool HAS_BIAS, int ACT>
+hipError_t launch_tm4(GemmParams gp, hipStream_t stream)
+{
+    gp.tiles_n = (gp.N + 32 * NWB - 1) / (32 * NWB);
+    gp.tiles_m = (gp.M + 32 * NXB - 1) / (32 * NXB);
+    gp.group_m = gp.tiles_m < 8 ? gp.tiles_m : 8;
+    hipLaunchKernelGGL((gemm4_bf16_nt_kernel<NXB, NWB, OUT_BF16, HAS_BIAS, ACT>), dim3(gp.tiles_m * gp.tiles_n),
+                       dim3(kThreads4), 0, stream, gp);
+    return hipGetLastError();
+}
+
 // One BM x BN output tile per workgroup (BM x 128 output columns with
 // SwiGLU, which always takes BN = 256: the tile's 256 weight rows are 128 gate and
 // 128 up rows).
@@ -581,6 +775,10 @@ hipError_t launch_tm(GemmParams gp, hipStream_t stream)
     return hipGetLastError();
 }
 
+// nxb x nwb in the eight-wave tile's terms (16-row blocks per wave, 32 nxb rows by 64 nwb
+// columns).  The 192- to 256-row tiles of the plain, bias and GELU epilogues run on four
+// waves (nwb = 4 or 3 becomes 8 or 6 column blocks per wave); the 64- and 128-row tiles and
+// SwiGLU run on eight.
 template <bool OUT_BF16, bool HAS_BIAS, int ACT>
 hipError_t launch_variant(const GemmParams &gp, int nxb, int nwb, hipStream_t stream)
 {
@@ -593,16 +791,22 @@ hipError_t launch_variant(const GemmParams &gp, int nxb, int nwb, hipStream_t st
                             : launch_tm<4, 4, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
         if (nwb == 3) {
             switch (nxb) {
-            case 6: return launch_tm<6, 3, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
-            case 7: return launch_tm<7, 3, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
-            default: return launch_tm<8, 3, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+            case 6: return launch_tm4<6, 6, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+            case 7: return launch_tm4<7, 6, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+            default: return launch_tm4<8, 6, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
             }
         }
-    }
-    switch (nxb) {
-    case 6: return launch_tm<6, 4, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
-    case 7: return launch_tm<7, 4, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
-    default: return launch_tm<8, 4, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+        switch (nxb) {
+        case 6: return launch_tm4<6, 8, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+        case 7: return launch_tm4<7, 8, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+        default: return launch_tm4<8, 8, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+        }
+    } else {
+        switch (nxb) {
+        case 6: return launch_tm<6, 4, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+        case 7: return launch_tm<7, 4, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+        default: return launch_tm<8, 4, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+        }
     }
 }
 
@@ -641,7 +845,7 @@ TileChoice pick_tile(int M, int N, int K, bool gated, int cus)
     TileChoice best{8, 4};
     double best_cost = -1;
     for (const Cand &cd : kCands) {
-        if ((gated && (cd.nwb != 4 || cd.nxb < 6)) || (cd.nxb == 7 && K < 3072))
+        if (gated && (cd.nwb != 4 || cd.nxb < 6 || (cd.nxb == 7 && K < 3072)))
             continue;
         const int bm = 32 * cd.nxb;
         const int cols = cd.nwb == 4 ? (gated ? 128 : 256) : 192;

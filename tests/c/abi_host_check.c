@@ -31,8 +31,8 @@ int main(void)
        weight-streaming kernel */
     CHECK(tp_linear_tile_shape(4608, 2304, 6144, TP_ACT_NONE, &r, &c) == TP_OK && r == 224 && c == 192,
           "tile shape 4608x2304x6144 is 224x192");
-    CHECK(tp_linear_tile_shape(4608, 6144, 768, TP_ACT_NONE, &r, &c) == TP_OK && r == 256 && c == 256,
-          "tile shape 4608x6144x768 is 256x256");
+    CHECK(tp_linear_tile_shape(4608, 6144, 768, TP_ACT_NONE, &r, &c) == TP_OK && r == 224 && c == 256,
+          "tile shape 4608x6144x768 is 224x256");
     CHECK(tp_linear_tile_shape(4, 9216, 6144, TP_ACT_NONE, &r, &c) == TP_OK && r == 0 && c == 0,
           "4 rows x 9216 x 6144 takes the weight-streaming kernel");
     CHECK(tp_linear_tile_shape(4, 9216, 6144, (tp_act)7, &r, &c) == TP_ERR_INVALID_ARG,

@@ -56,10 +56,12 @@ def test_no_kernel_spills_to_scratch(src, tmp_path):
 def test_every_gemm_instance_is_compiled_and_checked(tmp_path):
     """The tiled GEMM has 2 output types x bias or not, times 5 tile heights x 2 tile widths
     for each of the 2 plain epilogues (none, GELU) and 3 heights x 1 width for SwiGLU: 92
-    instances."""
+    instances.  The 192- to 256-row tiles of the plain epilogues (48 instances) are the
+    four-wave kernel, the 64- and 128-row tiles (32) and SwiGLU (12) the eight-wave one."""
     kernels = kernel_resources(os.path.join(CSRC, "gemm_bf16.hip"), tmp_path)
-    gemm = [n for n, _, _ in kernels if "gemm_bf16_nt_kernel" in n]
-    assert len(gemm) == 92, gemm
+    eight = [n for n, _, _ in kernels if "gemm_bf16_nt_kernel" in n]
+    four = [n for n, _, _ in kernels if "gemm4_bf16_nt_kernel" in n]
+    assert len(eight) == 44 and len(four) == 48, (eight, four)
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc is not installed")

@@ -5,14 +5,14 @@ oracle, through the C ABI.
 Ragged shapes span several tiles with partial tiles on both edges.  The
 kernel picks its tile shape per problem (64, 128, 192, 224 or 256 rows by 192
 or 256 columns, whichever needs the least time in rounds of tiles over the CUs;
-224 rows only for K >= 3072; tp_linear_tile_shape reports the choice).  On a
-256-CU device the RAGGED shapes with more than 128 rows and the first LARGE one
-run 64 x 192 tiles, the second LARGE one 224 x 192; the RAGGED shapes with 16
-to 64 rows take the split-K kernel, those with 1 and 5 rows the
-weight-streaming kernel.  TALL runs 224 x 256 tiles (504 in two
-rounds), so its last tile row is ragged inside a tile whose last X DMA
-instruction is issued by half the waves.  WIDE runs 256 x 256 tiles (256 in
-one round).  test_gpu_tiles.py reaches every tile shape with every epilogue.
+tp_linear_tile_shape reports the choice); the 192- to 256-row tiles run on four
+waves, the 64- and 128-row tiles on eight.  On a 256-CU device the RAGGED shapes
+with more than 128 rows and the first LARGE one run 64 x 192 tiles, the second
+LARGE one 224 x 192; the RAGGED shapes with 16 to 64 rows take the split-K
+kernel, those with 1 and 5 rows the weight-streaming kernel.  TALL runs
+224 x 256 tiles (504 in two rounds), so its last tile row is ragged.  WIDE
+runs 256 x 256 tiles (256 in one round).  test_gpu_tiles.py reaches every tile
+shape with every epilogue.
 Integer-valued inputs make every summation order exact, so there the GPU must
 equal the oracle bit for bit, which pins operand layout and indexing; random
 inputs are held to the stated tolerance and to the derived per-element bound.
@@ -360,11 +360,11 @@ def test_skinny_rows_per_wave(N):
         assert np.array_equal(dev_to_f64(y), oracle.colwise(c, w, b)), (N, B)
 
 
-# Two rounds of 256-row tiles (a short k loop keeps 224-row tiles out): the no-bias GELU and
-# SwiGLU epilogues at the largest register footprint of the kernel.  Sampled rows against
-# the oracle include every tile edge; the whole tensor must equal the same call with an
-# all-zero bias (another kernel instance, the same arithmetic per element).
-TALL256 = (4608, 6144, 128)
+# 256-row tiles: the no-bias GELU epilogue of the four-wave tiles and the SwiGLU epilogue of
+# the eight-wave tiles, each at its kernel's largest register footprint.  Sampled rows
+# against the oracle include every tile edge; the whole tensor must equal the same call with
+# an all-zero bias (another kernel instance, the same arithmetic per element).
+TALL256 = (2048, 6656, 128)
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])

@@ -38,7 +38,7 @@ def find_problem(rows, cols, act):
     best = None
     for K in (64, 3072):
         for M in (192, 224, 256, 300, 448, 672, 1000, 1344, 2048, 3072, 4608):
-            for N in (192, 256, 384, 576, 768, 1152, 1536, 2304, 3072, 4608, 6144):
+            for N in (192, 256, 384, 576, 768, 1152, 1536, 2304, 3072, 4608, 4864, 6144, 6656):
                 if M >= 2 * rows and N >= 2 * cols and tsl.tp_linear_tile_shape(M, N, K, act) == (rows, cols):
                     cost = M * N * K
                     if best is None or cost < best[0]:
@@ -116,3 +116,44 @@ def test_multistage_tiles_integer_exact(tile, M, N, K):
     assert torch.equal(y[:SUB_ROWS], y_sub)
     p = tsl.tp_linear_rowwise(xd, wd)
     assert np.array_equal(dev_to_f64(p[idx]), oracle.colwise(x, w, rows=srows))
+
+
+FOUR_WAVE = [(256, 256), (224, 256), (192, 256), (256, 192), (224, 192), (192, 192)]
+
+
+@pytest.mark.parametrize("rows,cols", FOUR_WAVE)
+def test_four_wave_tiles_every_k_tile_count(rows, cols):
+    """The 192- to 256-row tiles of the plain, bias and GELU epilogues run on four waves, one
+    per SIMD, whose pipeline has a prologue, a steady loop that loads the k-tile after next,
+    a loop for the last k-tiles and a final k32 step.  1, 2, 3, 5 and 20 k-tiles reach every
+    part.  Integer-valued operands make every summation order exact, so the output equals
+    the oracle bit for bit (bf16 output: the exact value rounded once), with and without
+    bias, on sampled rows (both rows of every tile edge) and all columns; M and N are ragged,
+    so the last tile row and column are partial.  GELU is checked on random normal operands
+    (where the stated tolerance applies) at 20 k-tiles."""
+    M, N, _ = find_problem(rows, cols, "none")
+    M, N = M - 3, N - 16
+    rng = np.random.default_rng(rows * 7 + cols)
+    srows = sample_rows(M, 8, seed=rows * cols, tile=rows)
+    idx = torch.from_numpy(srows).cuda()
+    for K in (64, 128, 192, 320, 1280):
+        assert tsl.tp_linear_tile_shape(M, N, K) == (rows, cols)
+        x = si.int_bf16(rng, (M, K), -4, 4)
+        w = si.int_bf16(rng, (N, K), -4, 4)
+        b = si.int_bf16(rng, (N,), -8, 8)
+        xd, wd, bd = bits_to_dev(x), bits_to_dev(w), bits_to_dev(b)
+        for bias in (False, True):
+            ref = oracle.colwise(x, w, b if bias else None, rows=srows)
+            what = f"{rows}x{cols} tile, {M}x{N}x{K} bias={bias}"
+            y32 = tsl.tp_linear_colwise(xd, wd, bd if bias else None, out_dtype=torch.float32)
+            assert np.array_equal(dev_to_f64(y32[idx]), ref), what + " fp32 out"
+            y16 = tsl.tp_linear_colwise(xd, wd, bd if bias else None)
+            assert np.array_equal(dev_to_f64(y16[idx]), oracle.bf16_widen(oracle.bf16_round(ref))), what + " bf16 out"
+        if K == 1280:
+            x = si.normal_bf16(rng, (M, K))
+            w = si.normal_bf16(rng, (N, K), 1 / np.sqrt(K))
+            b = si.normal_bf16(rng, (N,))
+            yg = tsl.tp_linear_colwise(bits_to_dev(x), bits_to_dev(w), bits_to_dev(b), act="gelu_tanh")
+            refg = oracle.colwise(x, w, b, act=oracle.ACT_GELU_TANH, rows=srows)
+            check_close(dev_to_f64(yg[idx]), refg, K, True, S=abs_dot(x[srows], w, b),
+                        what=f"{rows}x{cols} tile, {M}x{N}x{K} GELU")
