@@ -566,8 +566,12 @@ __device__ __forceinline__ void zero(f32x4 (&acc)[NXB][NWB])
 // loads are spread evenly over the step.  Issued in bursts after the first MFMAs instead,
 // the same kernel measured 3-9% slower than the eight-wave tiles; spread, and with the loads
 // in their scalar-base form (dma16_sbase), it measured 1-13% faster on every shape of the
-// DiT block (bit-identical outputs).  Pipeline, LDS layout, swizzle and epilogue are those of
-// the eight-wave kernel: 2 LDS stages, one barrier per k-tile before its second k32 step.
+// DiT block (bit-identical outputs); packing the loads into half of each step instead cost
+// 7%.  LDS layout, swizzle and epilogue are those of the eight-wave kernel, and so is the
+// pipeline of two LDS stages with one barrier per k-tile before its second k32 step.  The
+// 224 x 192 and 192 x 192 tiles fit three stages in the 160 KiB of LDS: a k-tile's loads
+// then spread over a whole k-tile and have twice as long to land (4608 x 4608 x 6144: 5%
+// faster than with two stages).
 constexpr int kThreads4 = 256;
 constexpr int kWaves4 = kThreads4 / 64;
 
@@ -590,7 +594,7 @@ __device__ __forceinline__ void dma16_sbase(const char *base, uint32_t off, uint
 
 // acc += X[m0 .. m0 + BM - 1, :] . W[n0 .. n0 + BN - 1, :]^T over all of K, four waves.
 // Rows past the end are clamped (computed and discarded).
-template <int NXB, int NWB>
+template <int NXB, int NWB, int S>
 __device__ __forceinline__ void mainloop4(const GemmParams &p, uint16_t *lds, const Ctx &c, int m0, int n0,
                                           f32x4 (&acc)[NXB][NWB])
 {
@@ -642,9 +646,11 @@ __device__ __forceinline__ void mainloop4(const GemmParams &p, uint16_t *lds, co
             f.w[r - NXB] = *reinterpret_cast<const bf16x8 *>(xs + kXElems + wrow_off + (r - NXB) * 16 * BK + cpos);
     };
     // One k32 step on `cur`; READS: the next step's fragments (stage rstage, k32 step rs) into
-    // `nxt`; DMA: the loads of the k-tile at dk0 into stage dstage.
-    auto step = [&](const Frags<NXB, NWB> &cur, Frags<NXB, NWB> &nxt, auto READS, auto DMA, int rstage, int rs,
-                    int dstage, int dk0) {
+    // `nxt`; loads [D0, D0 + DN) of the k-tile at dk0 into stage dstage, spread evenly.
+    auto step_part = [&](const Frags<NXB, NWB> &cur, Frags<NXB, NWB> &nxt, auto READS, auto D0, auto DN, int rstage,
+                         int rs, int dstage, int dk0) {
+        constexpr int d0 = decltype(D0)::value, dn = decltype(DN)::value;
+        constexpr int ds = dn > 0 ? kMfma / dn : 1;
 #pragma unroll
         for (int q = 0; q < kMfma; ++q) {
             const int j = q / NXB, i = q % NXB;  // W block by W block
@@ -652,9 +658,9 @@ __device__ __forceinline__ void mainloop4(const GemmParams &p, uint16_t *lds, co
                          : "+a"(acc[i][j])
                          : "v"(cur.w[j]), "v"(cur.x[i])
                          : "memory");
-            if constexpr (decltype(DMA)::value) {
-                if (q % DS == 1 % DS && q / DS < kDma)
-                    dma(q / DS, dstage, dk0);
+            if constexpr (dn > 0) {
+                if (q % ds == 1 % ds && q / ds < dn)
+                    dma(d0 + q / ds, dstage, dk0);
             }
             if constexpr (decltype(READS)::value) {
                 if (q % RS == 0 && q / RS < kReads)
@@ -662,43 +668,81 @@ __device__ __forceinline__ void mainloop4(const GemmParams &p, uint16_t *lds, co
             }
         }
     };
+    auto step = [&](const Frags<NXB, NWB> &cur, Frags<NXB, NWB> &nxt, auto READS, auto DMA, int rstage, int rs,
+                    int dstage, int dk0) {
+        step_part(cur, nxt, READS, std::integral_constant<int, 0>{},
+                  std::integral_constant<int, decltype(DMA)::value ? kDma : 0>{}, rstage, rs, dstage, dk0);
+    };
     using Yes = std::true_type;
     using No = std::false_type;
     const int T = p.K / BK;
     Frags<NXB, NWB> f0, f1;
-#pragma unroll
-    for (int d = 0; d < kDma; ++d)
-        dma(d, 0, 0);
-    wait_dma();
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < kReads; ++r)
-        read(r, 0, 0, f0);
-    if (T > 1) {
+    // Every iteration t computes k-tile t: step 0 on f0 while the step-1 fragments are read,
+    // the barrier (k-tile t + 1 landed, k-tile t read by every wave), step 1 on f1 while the
+    // next k-tile's step-0 fragments are read.  Past the last k-tile the loads repeat it into
+    // a stage that is never read again, and the last iteration reads fragments it does not
+    // use, so all iterations are the same one loop body: the compiler then has no reason to
+    // move an accumulator between registers between the MFMAs, where such a move could read a
+    // result before the MFMA has written it (the MFMAs are opaque to its hazard checks).
+    auto kt = [&](int u) { return min(u, T - 1) * BK; };
+    if constexpr (S == 3) {
+        // Three stages: k-tile u goes into stage u % 3, its first kH loads in step 1 of
+        // iteration u - 3, the rest in step 0 of iteration u - 2, so the loads of a k-tile are
+        // spread over a whole k-tile and land by the barrier of iteration u - 1; at that
+        // barrier only k-tile t + 2's loads may still be outstanding.
+        constexpr int kH = kDma / 2;
+        using I0 = std::integral_constant<int, 0>;
+        using IH = std::integral_constant<int, kH>;
+        using IR = std::integral_constant<int, kDma - kH>;
 #pragma unroll
         for (int d = 0; d < kDma; ++d)
-            dma(d, 1, BK);
+            dma(d, 0, 0);
+#pragma unroll
+        for (int d = 0; d < kDma; ++d)
+            dma(d, 1, kt(1));
+#pragma unroll
+        for (int d = 0; d < kH; ++d)
+            dma(d, 2, kt(2));
+        wait_dma_keep<kDma + kH>();
+        barrier_only();
+#pragma unroll
+        for (int r = 0; r < kReads; ++r)
+            read(r, 0, 0, f0);
+        int s0 = 0, s1 = 1, s2 = 2;  // stages of k-tiles t, t + 1, t + 2
+        int t = 0;
+        do {
+            step_part(f0, f1, Yes{}, IH{}, IR{}, s0, 1, s2, kt(t + 2));
+            wait_dma_keep<kDma>();
+            barrier_only();
+            step_part(f1, f0, Yes{}, I0{}, IH{}, s1, 0, s0, kt(t + 3));
+            const int sn = s0;
+            s0 = s1;
+            s1 = s2;
+            s2 = sn;
+        } while (++t < T);
+    } else {
+        // Two stages: stage t % 2 holds k-tile t; step 1 loads k-tile t + 2 into it.
+#pragma unroll
+        for (int d = 0; d < kDma; ++d)
+            dma(d, 0, 0);
+#pragma unroll
+        for (int d = 0; d < kDma; ++d)
+            dma(d, 1, kt(1));
+        wait_dma_keep<kDma>();
+        barrier_only();
+#pragma unroll
+        for (int r = 0; r < kReads; ++r)
+            read(r, 0, 0, f0);
+        int t = 0;
+        do {
+            const int st = t & 1;
+            step(f0, f1, Yes{}, No{}, st, 1, 0, 0);
+            wait_dma_keep<0>();
+            barrier_only();
+            step(f1, f0, Yes{}, Yes{}, st ^ 1, 0, st, kt(t + 2));
+        } while (++t < T);
     }
-    // Stage t % 2 holds k-tile t.  Step 0 runs on f0 while the step-1 fragments are read; the
-    // barrier then finds k-tile t + 1 landed and stage t % 2 read by every wave, so step 1
-    // loads k-tile t + 2 into it while it reads the next k-tile's step-0 fragments.
-    int t = 0;
-    for (; t < T - 2; ++t) {
-        const int st = t & 1;
-        step(f0, f1, Yes{}, No{}, st, 1, 0, 0);
-        wait_dma();
-        __syncthreads();
-        step(f1, f0, Yes{}, Yes{}, st ^ 1, 0, st, (t + 2) * BK);
-    }
-    for (; t < T - 1; ++t) {
-        const int st = t & 1;
-        step(f0, f1, Yes{}, No{}, st, 1, 0, 0);
-        wait_dma();
-        __syncthreads();
-        step(f1, f0, Yes{}, No{}, st ^ 1, 0, 0, 0);
-    }
-    step(f0, f1, Yes{}, No{}, (T - 1) & 1, 1, 0, 0);
-    step(f1, f0, No{}, No{}, 0, 0, 0, 0);
+    wait_dma();  // the repeated loads of the last k-tile, before the epilogue reuses the LDS
     // The last MFMAs' results must be written before they are read as ordinary values; the
     // empty statements keep every read of an accumulator after the wait.
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -717,7 +761,9 @@ void gemm4_bf16_nt_kernel(GemmParams p)
     static_assert(ACT != kActSwiglu, "the gated epilogue runs on the eight-wave tiles");
     static_assert(NXB >= 6 && NXB <= 8 && (NWB == 6 || NWB == 8), "192-256 rows by 192 or 256 columns");
     constexpr int BM = 32 * NXB, BN = 32 * NWB;
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * (BM + BN) * BK];
+    // three stages where they fit in the 160 KiB of LDS (224 x 192 and 192 x 192 tiles)
+    constexpr int S = 3 * (BM + BN) * BK * 2 <= 160 * 1024 ? 3 : 2;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[S * (BM + BN) * BK];
     Ctx c;
     c.lane = threadIdx.x & 63;
     c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -727,7 +773,7 @@ void gemm4_bf16_nt_kernel(GemmParams p)
     tile_of(xcd_contiguous(blockIdx.x, p.tiles_m * p.tiles_n), p, tm, tn);
     f32x4 acc[NXB][NWB];
     zero<NXB, NWB>(acc);
-    mainloop4<NXB, NWB>(p, lds, c, tm * BM, tn * BN, acc);
+    mainloop4<NXB, NWB, S>(p, lds, c, tm * BM, tn * BN, acc);
     epilogue<NXB, NWB, OUT_BF16, HAS_BIAS, ACT>(p, lds, c, tm * BM, tn * BN, acc);
 }
 

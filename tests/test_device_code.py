@@ -73,3 +73,31 @@ def test_every_split_k_instance_is_compiled_and_checked(tmp_path):
     narrow = [(n, p) for n, p, _ in kernels if "gemm_narrow_kernel" in n]
     assert len(narrow) == 168, [n for n, _ in narrow]
     assert all(p == 0 for _, p in narrow)
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc is not installed")
+def test_four_wave_gemm_moves_no_accumulator_among_its_mfmas(tmp_path):
+    """The four-wave GEMM writes its MFMAs as inline assembly, so the compiler's hazard checks
+    do not see them: an accumulator read, written or moved by a compiler-made instruction
+    between the first MFMA and the wait that follows the last one could see a result the MFMA
+    has not written yet.  The kernel's single uniform loop body leaves the compiler no reason
+    for such a move; this checks every instance's device assembly for one."""
+    from tensor_sharded_linear_amd.build import FLAGS
+    flags = [f for f in FLAGS if f not in ("-shared", "-fPIC")]
+    out = tmp_path / "gemm_bf16.s"
+    cmd = [HIPCC, *flags, "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           os.path.join(CSRC, "gemm_bf16.hip"), "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    text = out.read_text()
+    checked, bad = 0, []
+    for m in re.finditer(r"^(\S*gemm4_bf16_nt_kernel\S*):", text, re.M):
+        body = text[m.end():text.index("s_endpgm", m.end())].splitlines()
+        first = next(i for i, line in enumerate(body) if "v_mfma" in line)
+        wait = next(i for i, line in enumerate(body) if "s_nop 7" in line and i > first)
+        moves = [line.strip() for line in body[first:wait] if re.search(r"v_accvgpr_(read|write|mov)", line)]
+        checked += 1
+        if moves:
+            bad.append((m.group(1), len(moves), moves[:2]))
+    assert checked == 48, checked
+    assert not bad, bad
