@@ -74,15 +74,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define TPL_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
-// The tile shape is two template parameters, the 16-row MFMA blocks per wave NXB = 8, 7,
-// 6, 4 or 2 (256, 224, 192, 128 or 64 rows) and the 16-column blocks per wave NWB = 4 or 3
-// (256 or 192 columns); pick_tile chooses the one that fills the CUs best for the shape.
+// The tile shape is two template parameters, the 16-row MFMA blocks per wave NXB and the
+// 16-column blocks per wave NWB.  Eight-wave tiles (2 x 4 waves): NXB = 4 or 2 (128 or 64
+// rows) by NWB = 4 or 3 (256 or 192 columns).  Four-wave tiles (2 x 2 waves, mainloop4):
+// NXB = 8, 7 or 6 (256, 224 or 192 rows) by NWB = 8 or 6 (256 or 192 columns).  pick_tile
+// chooses the shape that fills the CUs best for the problem.
 constexpr int BK = 64;
 constexpr int kThreads = 512;     // 8 waves in a 2 (M) x 4 (N) grid
 constexpr int kWavesN = 4;
 constexpr int kWaves = kThreads / 64;
 
-// NWB = 16-row W blocks (16-column MFMA tiles) per wave: 4 or 3, for 256- or 192-column tiles.
+// An eight-wave tile; WM and WN (a wave's rows and columns) also serve the shared epilogue.
 template <int NXB, int NWB>
 struct Tile {
     static constexpr int XB = NXB;       // 16-row X blocks (16-row MFMA tiles) per wave
@@ -93,19 +95,13 @@ struct Tile {
     static constexpr int BN = kWavesN * WN;  // columns of the output tile (weight rows)
     static constexpr int kDmaW = (BN * BK * 2) / (kThreads * 16);  // 16-byte DMAs per thread per W tile
     static constexpr int kXElems = BM * BK;
-    // 16-byte DMAs per thread per X tile.  One DMA instruction of the
-    // workgroup moves 64 rows; with an odd NXB the last one covers 32 rows and
-    // only waves 0-3 issue it.
-    static constexpr int kDmaX = (BM + 63) / 64;
-    static constexpr bool kDmaXPartial = BM % 64 != 0;
+    static constexpr int kDmaX = BM / 64;  // one DMA instruction of the workgroup moves 64 rows
     static constexpr int kStageElems = (BM + BN) * BK;  // X tile + W tile
-    // 64- and 128-row tiles stream a weight panel for few rows and keep more k-tiles in
-    // flight: 64 x 192 4 stages (128 KiB), 64 x 256 3 (120 KiB), 128 x 192 3 (120 KiB),
-    // 128 x 256 3 (144 KiB).  The larger tiles double buffer (128, 120 or 112 KiB): there
-    // the MFMA work of a k-tile covers the loads of the next.
-    static constexpr int kStages = NXB == 2 ? (NWB == 3 ? 4 : 3) : (NXB == 4 ? 3 : 2);
+    // These tiles stream a weight panel for few rows and keep more k-tiles in flight:
+    // 64 x 192 4 stages (128 KiB), 64 x 256 3 (120 KiB), 128 x 192 3 (120 KiB), 128 x 256 3
+    // (144 KiB); a k loop shorter than the stages double buffers.
+    static constexpr int kStages = NXB == 2 ? (NWB == 3 ? 4 : 3) : 3;
     static constexpr int kLdsElems = kStages * kStageElems;
-    static_assert(BM % 32 == 0, "X tile rows: a multiple of 32");
 };
 
 struct GemmParams {
@@ -234,14 +230,10 @@ __device__ __forceinline__ void dma16(const char *src, uint16_t *dst)
 }
 
 // acc += X[m0 .. m0+BM-1, k] . Wt^T over k-tiles [kt0, kt1), where the BN
-// rows of the W tile Wt are W[n0 .. n0+BN-1] or, GATED (BN = 256), 32-row blocks taken in
-// turn from the gate half W[0 .. N) and the up half W[N .. 2N) of a packed
-// [gate; up] weight: tile row 64 q + 32 h + i is W[h N + n0 + 32 q + i], so
-// wave q's 16-column MFMA blocks 0, 1 hold the gate and blocks 2, 3 the up
-// projection of the same 32 output columns n0 + 32 q + [0, 32).  Rows past the end are clamped
-// (computed and discarded).  Starts with a barrier, so the LDS may still be in
-// use by the caller's previous tile when it is called.
-template <int NXB, int NWB, bool GATED>
+// rows of the W tile Wt are W[n0 .. n0+BN-1] (eight waves: the 64- and 128-row tiles).
+// Rows past the end are clamped (computed and discarded).  Starts with a barrier, so the
+// LDS may still be in use by the caller's previous tile when it is called.
+template <int NXB, int NWB>
 __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, const Ctx &c, int m0, int n0,
                                          int kt0, int kt1, f32x4 (&acc)[NXB][NWB])
 {
@@ -250,7 +242,6 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
     const char *xbase = reinterpret_cast<const char *>(p.x) + (int64_t)kt0 * BK * 2;
     const char *wbase = reinterpret_cast<const char *>(p.w) + (int64_t)kt0 * BK * 2;
     typedef Tile<NXB, NWB> L;
-    static_assert(!GATED || NWB == 4, "the gated tile pairs two gate and two up blocks per wave");
     constexpr int WB = NWB, kDmaW = L::kDmaW;
     static_assert(kDmaW * kWaves * 512 == L::BN * BK, "the W DMAs cover the W tile exactly");
     static_assert(L::kDmaX * kWaves * 512 >= L::kXElems, "the X DMAs cover the X tile");
@@ -263,8 +254,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
 #pragma unroll
     for (int j = 0; j < kDmaW; ++j) {
         // DMA instruction j fills tile rows 64 j + dma_row
-        const int gn = GATED ? (c.dma_row >> 5) * p.N + min(n0 + 32 * j + (c.dma_row & 31), p.N - 1)
-                             : min(n0 + j * (8 * kWaves) + c.dma_row, p.N - 1);
+        const int gn = min(n0 + j * (8 * kWaves) + c.dma_row, p.N - 1);
         woff[j] = (uint32_t)(((int64_t)gn * p.ldw + c.dma_chunk * 8) * 2);
     }
     auto issue = [&](int stage, int k0) {
@@ -274,52 +264,29 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
         const char *wb = wbase + k0 * 2;
 #pragma unroll
         for (int j = 0; j < L::kDmaX; ++j)
-            if (!L::kDmaXPartial || j < L::kDmaX - 1 || (j * kWaves + c.wave) * 512 < L::kXElems)
-                dma16(xb + xoff[j], xs + (j * kWaves + c.wave) * 512);
+            dma16(xb + xoff[j], xs + (j * kWaves + c.wave) * 512);
 #pragma unroll
         for (int j = 0; j < kDmaW; ++j)
             dma16(wb + woff[j], ws + (j * kWaves + c.wave) * 512);
     };
-    // 256-row tiles run their MFMAs W block by W block, the other heights X block by X
-    // block (each order measured the faster one for its heights in the bench step), and the
-    // fragments are read in the order the MFMAs use them.
-    constexpr bool kLoadsInterleaved = NXB == 8;
+    // The MFMAs run X block by X block, and the fragments are read in the order they use them.
     auto read_frags = [&](int stage, int s, Frags<NXB, NWB> &f) {
         const uint16_t *xs = lds + stage * L::kStageElems;
         const uint16_t *ws = xs + L::kXElems;
         const int cpos = ((s * 4 + c.kh) ^ c.swz) * 8;
-        auto rx = [&]() {
 #pragma unroll
-            for (int i = 0; i < L::XB; ++i)
-                f.x[i] = *reinterpret_cast<const bf16x8 *>(xs + c.xrow_off + i * 16 * BK + cpos);
-        };
-        auto rw = [&]() {
+        for (int i = 0; i < L::XB; ++i)
+            f.x[i] = *reinterpret_cast<const bf16x8 *>(xs + c.xrow_off + i * 16 * BK + cpos);
 #pragma unroll
-            for (int j = 0; j < WB; ++j)
-                f.w[j] = *reinterpret_cast<const bf16x8 *>(ws + c.wrow_off + j * 16 * BK + cpos);
-        };
-        if constexpr (kLoadsInterleaved) {
-            rw();
-            rx();
-        } else {
-            rx();
-            rw();
-        }
+        for (int j = 0; j < WB; ++j)
+            f.w[j] = *reinterpret_cast<const bf16x8 *>(ws + c.wrow_off + j * 16 * BK + cpos);
     };
     auto mma = [&](const Frags<NXB, NWB> &f) {
-        if constexpr (kLoadsInterleaved) {
+#pragma unroll
+        for (int i = 0; i < L::XB; ++i)
 #pragma unroll
             for (int j = 0; j < WB; ++j)
-#pragma unroll
-                for (int i = 0; i < L::XB; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.w[j], f.x[i], acc[i][j], 0, 0, 0);
-        } else {
-#pragma unroll
-            for (int i = 0; i < L::XB; ++i)
-#pragma unroll
-                for (int j = 0; j < WB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.w[j], f.x[i], acc[i][j], 0, 0, 0);
-        }
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.w[j], f.x[i], acc[i][j], 0, 0, 0);
     };
     // Pipeline: stage t % 2 holds k-tile t; steps s = 0, 1 are its k32 slices.
     // TPL_STEP(read next, mma current) fixes the order of one step for the
@@ -332,19 +299,6 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
         }                                                                     \
         __builtin_amdgcn_sched_group_barrier(0x008, L::XB * WB - (L::XB + WB), 0); \
         __builtin_amdgcn_sched_barrier(0); } while (0)
-    // Like TPL_STEP, with the loads of a k-tile issued first, one after each of the first
-    // MFMAs, instead of in a burst before them.
-#define TPL_STEP_DMA(DM, RD, MM) do { DM; RD; MM;                              \
-        _Pragma("unroll") for (int g_ = 0; g_ < L::kDmaX + kDmaW; ++g_) {     \
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                \
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                \
-        }                                                                     \
-        _Pragma("unroll") for (int g_ = 0; g_ < L::XB + WB; ++g_) {           \
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                \
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                \
-        }                                                                     \
-        __builtin_amdgcn_sched_group_barrier(0x008, L::XB * WB - (L::XB + WB) - (L::kDmaX + kDmaW), 0); \
-        __builtin_amdgcn_sched_barrier(0); } while (0)
     const int T = kt1 - kt0;
     Frags<NXB, NWB> f0, f1;
     if constexpr (L::kStages > 2) {
@@ -355,7 +309,6 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
             // being computed.
             constexpr int S = L::kStages;
             constexpr int kPer = L::kDmaX + kDmaW;  // DMA instructions per k-tile and wave
-            static_assert(!L::kDmaXPartial, "every wave issues the same loads per k-tile");
             static_assert((S - 1) * kPer <= 63, "the wait count fits vmcnt");
             __syncthreads();  // the LDS is free: the previous tile's reads are done
 #pragma unroll
@@ -392,18 +345,6 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
     if (T > 1)
         issue(1, BK);
     int t = 0;
-    if constexpr (kLoadsInterleaved) {
-        // k-tiles whose successor-but-one exists: its loads go out one per MFMA at the start
-        // of the second k32 step, ahead of the fragment reads (256-row tiles: the burst of
-        // loads before the step left the MFMA pipe idle; 2-3% on the short-K rowwise shapes)
-        for (; t < T - 2; ++t) {
-            const int st = t & 1;
-            TPL_STEP(read_frags(st, 1, f1), mma(f0));
-            wait_dma();
-            __syncthreads();
-            TPL_STEP_DMA(issue(st, (t + 2) * BK), read_frags(st ^ 1, 0, f0), mma(f1));
-        }
-    }
     for (; t < T - 1; ++t) {
         const int st = t & 1;
         TPL_STEP(read_frags(st, 1, f1), mma(f0));
@@ -415,11 +356,10 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, uint16_t *lds, con
     }
     TPL_STEP(read_frags((T - 1) & 1, 1, f1), mma(f0));
     mma(f1);
-    // Keep the epilogue's arithmetic out of the last MFMAs: interleaved with
-    // them, the 256-row GELU and SwiGLU tiles ran out of registers and spilled.
+    // Keep the epilogue's arithmetic out of the last MFMAs (interleaved with them, tiles at
+    // the register limit spilled).
     __builtin_amdgcn_sched_barrier(0);
 #undef TPL_STEP
-#undef TPL_STEP_DMA
 }
 
 // SiLU (Swish): v * sigmoid(v) = v / (1 + exp(-v)) = v / (1 + 2^(-v log2(e))),
@@ -433,15 +373,15 @@ __device__ __forceinline__ float silu(float v)
 // Epilogue activations.
 constexpr int kActNone = 0;
 constexpr int kActGelu = 1;
-constexpr int kActSwiglu = 2;  // W tile = interleaved [gate; up] 32-row blocks, see mainloop
+constexpr int kActSwiglu = 2;  // W tile = interleaved [gate; up] 64-row blocks, see mainloop4
 
 // Epilogue through LDS.  Lane l holds Y[m][n..n+3] for m = row base +
 // 16 i + l%16 and n = column base + 16 j + 4 (l / 16).  For each of the
 // wave's 16-row slices the wave writes its output values (after bias /
 // activation / rounding) into a private LDS area with padded rows, then
-// reads them back row-major and stores whole row segments.  A wave owns 64
-// output columns, or 32 with SwiGLU: there its blocks j = 0, 1 hold the gate
-// and j = 2, 3 the up projection of the same 32 columns, and the output is
+// reads them back row-major and stores whole row segments.  A wave owns 16 NWB
+// output columns, or 8 NWB with SwiGLU: there its blocks j < NWB / 2 hold the gate
+// and j >= NWB / 2 the up projection of the same columns, and the output is
 // silu(gate + b_gate) * (up + b_up), the bias being [b_gate; b_up] (2 N).
 template <int NXB, int NWB, bool OUT_BF16, bool HAS_BIAS, int ACT>
 __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, const Ctx &c, int m0, int n0,
@@ -450,7 +390,7 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, con
     __syncthreads();  // every wave is done reading the operand stages
     typedef typename std::conditional<OUT_BF16, __bf16, float>::type OutT;
     constexpr bool kGated = ACT == kActSwiglu;
-    static_assert(!kGated || NWB == 4, "the gated epilogue pairs two gate and two up blocks");
+    static_assert(!kGated || NWB == 4 || NWB == 8, "the gated epilogue pairs NWB / 2 gate and up blocks");
     constexpr int WNO = kGated ? Tile<NXB, NWB>::WN / 2 : Tile<NXB, NWB>::WN;  // output columns per wave
     constexpr int JO = WNO / 16;               // 16-column output blocks per wave
     constexpr int kOutEs = sizeof(OutT);
@@ -493,7 +433,7 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, uint16_t *lds, con
                 v[3] = gelu_tanh(v[3]);
             }
             if (kGated) {
-                f32x4 u = acc[i][j + 2];
+                f32x4 u = acc[i][j + NWB / 2];
                 if (HAS_BIAS && n < p.N)
                     u = u + bias4(p.N + n);
                 v[0] = silu(v[0]) * u[0];
@@ -594,10 +534,11 @@ __device__ __forceinline__ void dma16_sbase(const char *base, uint32_t off, uint
 
 // acc += X[m0 .. m0 + BM - 1, :] . W[n0 .. n0 + BN - 1, :]^T over all of K, four waves.
 // Rows past the end are clamped (computed and discarded).
-template <int NXB, int NWB, int S>
+template <int NXB, int NWB, int S, bool GATED>
 __device__ __forceinline__ void mainloop4(const GemmParams &p, uint16_t *lds, const Ctx &c, int m0, int n0,
                                           f32x4 (&acc)[NXB][NWB])
 {
+    static_assert(!GATED || NWB == 8, "the gated tile pairs four gate and four up blocks per wave");
     constexpr int WM = 16 * NXB, WN = 16 * NWB, BM = 2 * WM, BN = 2 * WN;
     constexpr int kDmaX = BM / 32, kDmaW = BN / 32, kDma = kDmaX + kDmaW;  // per lane and k-tile
     constexpr int kXElems = BM * BK, kStageElems = (BM + BN) * BK;
@@ -623,7 +564,10 @@ __device__ __forceinline__ void mainloop4(const GemmParams &p, uint16_t *lds, co
     }
 #pragma unroll
     for (int j = 0; j < kDmaW; ++j) {
-        const int gn = min(n0 + 32 * j + dma_row, p.N - 1);
+        // GATED: tile row 128 q + 64 h + i is W[h N + n0 + 64 q + i], so wave column q's blocks
+        // 0-3 hold the gate rows and blocks 4-7 the up rows of outputs n0 + 64 q + [0, 64).
+        const int gn = GATED ? ((j >> 1) & 1) * p.N + min(n0 + 64 * (j >> 2) + 32 * (j & 1) + dma_row, p.N - 1)
+                             : min(n0 + 32 * j + dma_row, p.N - 1);
         woff[j] = (uint32_t)(((int64_t)gn * p.ldw + dma_chunk * 8) * 2);
     }
     const char *xbase = reinterpret_cast<const char *>(p.x);
@@ -758,9 +702,10 @@ template <int NXB, int NWB, bool OUT_BF16, bool HAS_BIAS, int ACT>
 __global__ __launch_bounds__(kThreads4) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm4_bf16_nt_kernel(GemmParams p)
 {
-    static_assert(ACT != kActSwiglu, "the gated epilogue runs on the eight-wave tiles");
     static_assert(NXB >= 6 && NXB <= 8 && (NWB == 6 || NWB == 8), "192-256 rows by 192 or 256 columns");
+    constexpr bool kGated = ACT == kActSwiglu;
     constexpr int BM = 32 * NXB, BN = 32 * NWB;
+    constexpr int kTileCols = kGated ? BN / 2 : BN;  // SwiGLU: 128 gate and 128 up weight rows
     // three stages where they fit in the 160 KiB of LDS (224 x 192 and 192 x 192 tiles)
     constexpr int S = 3 * (BM + BN) * BK * 2 <= 160 * 1024 ? 3 : 2;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[S * (BM + BN) * BK];
@@ -773,14 +718,15 @@ void gemm4_bf16_nt_kernel(GemmParams p)
     tile_of(xcd_contiguous(blockIdx.x, p.tiles_m * p.tiles_n), p, tm, tn);
     f32x4 acc[NXB][NWB];
     zero<NXB, NWB>(acc);
-    mainloop4<NXB, NWB, S>(p, lds, c, tm * BM, tn * BN, acc);
-    epilogue<NXB, NWB, OUT_BF16, HAS_BIAS, ACT>(p, lds, c, tm * BM, tn * BN, acc);
+    mainloop4<NXB, NWB, S, kGated>(p, lds, c, tm * BM, tn * kTileCols, acc);
+    epilogue<NXB, NWB, OUT_BF16, HAS_BIAS, ACT>(p, lds, c, tm * BM, tn * kTileCols, acc);
 }
 
 template <int NXB, int NWB, bool OUT_BF16, bool HAS_BIAS, int ACT>
 hipError_t launch_tm4(GemmParams gp, hipStream_t stream)
 {
-    gp.tiles_n = (gp.N + 32 * NWB - 1) / (32 * NWB);
+    const int tile_cols = ACT == kActSwiglu ? 16 * NWB : 32 * NWB;
+    gp.tiles_n = (gp.N + tile_cols - 1) / tile_cols;
     gp.tiles_m = (gp.M + 32 * NXB - 1) / (32 * NXB);
     gp.group_m = gp.tiles_m < 8 ? gp.tiles_m : 8;
     hipLaunchKernelGGL((gemm4_bf16_nt_kernel<NXB, NWB, OUT_BF16, HAS_BIAS, ACT>), dim3(gp.tiles_m * gp.tiles_n),
@@ -788,32 +734,29 @@ hipError_t launch_tm4(GemmParams gp, hipStream_t stream)
     return hipGetLastError();
 }
 
-// One BM x BN output tile per workgroup (BM x 128 output columns with
-// SwiGLU, which always takes BN = 256: the tile's 256 weight rows are 128 gate and
-// 128 up rows).
+// One BM x BN output tile per workgroup of eight waves (the 64- and 128-row tiles).
 template <int NXB, int NWB, bool OUT_BF16, bool HAS_BIAS, int ACT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_nt_kernel(GemmParams p)
 {
     typedef Tile<NXB, NWB> L;
-    constexpr bool kGated = ACT == kActSwiglu;
-    constexpr int kTileCols = kGated ? L::BN / 2 : L::BN;
+    static_assert(ACT != kActSwiglu, "the gated epilogue runs on the four-wave tiles");
+    static_assert(NXB == 2 || NXB == 4, "64- and 128-row tiles");
     __shared__ __attribute__((aligned(1024))) uint16_t lds[L::kLdsElems];
     const Ctx c = make_ctx<NXB, NWB>();
     int tm, tn;
     tile_of(xcd_contiguous(blockIdx.x, p.tiles_m * p.tiles_n), p, tm, tn);
     f32x4 acc[NXB][NWB];
     zero<NXB, NWB>(acc);
-    mainloop<NXB, NWB, kGated>(p, lds, c, tm * L::BM, tn * kTileCols, 0, p.K / BK, acc);
-    epilogue<NXB, NWB, OUT_BF16, HAS_BIAS, ACT>(p, lds, c, tm * L::BM, tn * kTileCols, acc);
+    mainloop<NXB, NWB>(p, lds, c, tm * L::BM, tn * L::BN, 0, p.K / BK, acc);
+    epilogue<NXB, NWB, OUT_BF16, HAS_BIAS, ACT>(p, lds, c, tm * L::BM, tn * L::BN, acc);
 }
 
 template <int NXB, int NWB, bool OUT_BF16, bool HAS_BIAS, int ACT>
 hipError_t launch_tm(GemmParams gp, hipStream_t stream)
 {
     typedef Tile<NXB, NWB> L;
-    const int tile_cols = ACT == kActSwiglu ? L::BN / 2 : L::BN;
-    gp.tiles_n = (gp.N + tile_cols - 1) / tile_cols;
+    gp.tiles_n = (gp.N + L::BN - 1) / L::BN;
     gp.tiles_m = (gp.M + L::BM - 1) / L::BM;
     gp.group_m = gp.tiles_m < 8 ? gp.tiles_m : 8;
     hipLaunchKernelGGL((gemm_bf16_nt_kernel<NXB, NWB, OUT_BF16, HAS_BIAS, ACT>), dim3(gp.tiles_m * gp.tiles_n),
@@ -848,10 +791,11 @@ hipError_t launch_variant(const GemmParams &gp, int nxb, int nwb, hipStream_t st
         default: return launch_tm4<8, 8, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
         }
     } else {
+        (void)nwb;  // SwiGLU tiles are 256 weight rows = 128 outputs wide
         switch (nxb) {
-        case 6: return launch_tm<6, 4, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
-        case 7: return launch_tm<7, 4, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
-        default: return launch_tm<8, 4, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+        case 6: return launch_tm4<6, 8, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+        case 7: return launch_tm4<7, 8, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
+        default: return launch_tm4<8, 8, OUT_BF16, HAS_BIAS, ACT>(gp, stream);
         }
     }
 }
@@ -891,7 +835,7 @@ TileChoice pick_tile(int M, int N, int K, bool gated, int cus)
     TileChoice best{8, 4};
     double best_cost = -1;
     for (const Cand &cd : kCands) {
-        if (gated && (cd.nwb != 4 || cd.nxb < 6 || (cd.nxb == 7 && K < 3072)))
+        if (gated && (cd.nwb != 4 || cd.nxb < 6))
             continue;
         const int bm = 32 * cd.nxb;
         const int cols = cd.nwb == 4 ? (gated ? 128 : 256) : 192;

@@ -318,8 +318,8 @@ def test_tile_shape_query():
     assert q(4608, 6144, 768) == (224, 256)               # 504 tiles, 1.97 rounds
     assert q(4608, 6144, 128, "gelu_tanh") == (224, 256)
     assert q(2048, 6656, 128, "gelu_tanh") == (256, 256)  # 208 tiles, one round
-    assert q(4608, 3072, 128, "swiglu") == (256, 128)     # 128 outputs per SwiGLU tile; 224 rows
-    assert q(4608, 3072, 3072, "swiglu") == (224, 128)    # only for K >= 3072 there
+    assert q(4608, 3072, 128, "swiglu") == (224, 128)     # 128 outputs per SwiGLU tile
+    assert q(960, 6656, 128, "swiglu") == (256, 128)
     assert q(0, 16, 64)[0] in (0, 192, 224, 256)
     with pytest.raises(ValueError):
         q(-1, 16, 64)

@@ -5,8 +5,8 @@ oracle, through the C ABI.
 Ragged shapes span several tiles with partial tiles on both edges.  The
 kernel picks its tile shape per problem (64, 128, 192, 224 or 256 rows by 192
 or 256 columns, whichever needs the least time in rounds of tiles over the CUs;
-tp_linear_tile_shape reports the choice); the 192- to 256-row tiles run on four
-waves, the 64- and 128-row tiles on eight.  On a 256-CU device the RAGGED shapes
+tp_linear_tile_shape reports the choice); the 192- to 256-row tiles (SwiGLU
+always) run on four waves, the 64- and 128-row tiles on eight.  On a 256-CU device the RAGGED shapes
 with more than 128 rows and the first LARGE one run 64 x 192 tiles, the second
 LARGE one 224 x 192; the RAGGED shapes with 16 to 64 rows take the split-K
 kernel, those with 1 and 5 rows the weight-streaming kernel.  TALL runs
@@ -360,8 +360,8 @@ def test_skinny_rows_per_wave(N):
         assert np.array_equal(dev_to_f64(y), oracle.colwise(c, w, b)), (N, B)
 
 
-# 256-row tiles: the no-bias GELU epilogue of the four-wave tiles and the SwiGLU epilogue of
-# the eight-wave tiles, each at its kernel's largest register footprint.  Sampled rows
+# 256-row tiles: the no-bias GELU and SwiGLU epilogues at the largest register footprint of
+# the four-wave kernel.  Sampled rows
 # against the oracle include every tile edge; the whole tensor must equal the same call with
 # an all-zero bias (another kernel instance, the same arithmetic per element).
 TALL256 = (2048, 6656, 128)
@@ -387,7 +387,7 @@ def test_gelu_no_bias_256_row_tiles(out):
 
 
 def test_swiglu_no_bias_256_row_tiles():
-    M, n, K = 4608, 3072, 128
+    M, n, K = 960, 6656, 128
     assert tsl.tp_linear_tile_shape(M, n, K, "swiglu") == (256, 128)
     rng = np.random.default_rng(42)
     x = si.normal_bf16(rng, (M, K))
