@@ -12,47 +12,45 @@
 //  * BM x BN output tile per workgroup: 256, 224 or 192 rows by 256 or 192
 //    columns for many rows, 128 or 64 rows for a few hundred, whichever fills
 //    the CUs best (pick_tile); up to 128 rows the split-K kernel
-//    (gemm_narrow.hip) runs instead.  K step 64, 512 threads = 8
-//    waves in a 2 (M) x 4 (N) grid; each wave owns a (BM/2) x (BN/4) sub-tile
-//    held as NXB x NWB MFMA 16x16 fp32 accumulators (at most 128 accumulator
-//    registers per lane).  Two waves per SIMD, so one wave's LDS fragment reads
-//    overlap the other's MFMAs.
-//  * On dense random operands the part runs at its power limit.  Counters on
-//    this kernel (MFMA-busy cycles over GUI-active cycles, and GUI-active
-//    cycles over time) show the MFMA pipe busy 64-66% of cycles with random,
-//    constant or all-zero operands alike, while the clock falls from 2.41 GHz
-//    (zeros) to 1.76 GHz (random) back to back; changes to this schedule that
-//    raised the busy fraction lowered the clock by as much, so the fill of the
-//    CUs sets its speed.  (A vendor kernel of 4 waves, one per SIMD, keeps the
-//    pipe 79-85% busy under the same cap on products its 256 x 256 tiles fill
-//    in whole rounds; 4-wave versions of this kernel measured 1-12% slower.)
-//    Counting operand reads plus accumulator read and write, the 16x16x32
-//    form moves 20% fewer register bytes per flop than 32x32x16, and it
-//    measured 3-9% faster on every workload shape.
+//    (gemm_narrow.hip) runs instead.  K step 64.
+//  * The 192- to 256-row tiles run on 256 threads = 4 waves in a 2 x 2 grid,
+//    one wave per SIMD, each owning (BM/2) x (BN/2) outputs as up to 8 x 8 MFMA
+//    16x16 fp32 accumulators in the accumulation registers (mainloop4).  Per
+//    k32 step a wave reads NXB + NWB fragments for NXB x NWB MFMAs (16 for 64
+//    at 256 x 256), a third fewer LDS reads per flop than eight waves of
+//    128 x 64.  The 64- and 128-row tiles run on 512 threads = 8 waves in a
+//    2 x 4 grid, two per SIMD (mainloop).
+//  * On dense random operands the part runs at its power limit (the clock
+//    falls from 2.41 GHz on all-zero operands to 1.76 GHz on random ones at
+//    the same MFMA-busy fraction), so energy per flop and the MFMA-busy
+//    fraction under the cap set the speed.  The four-wave schedule writes out
+//    every k32 step: MFMAs with the fragment reads and loads spread evenly
+//    between them; bursts of loads left the single wave of a SIMD stalled on
+//    issue.  The 16x16x32 form moves 20% fewer register bytes per flop than
+//    32x32x16 (operand reads plus accumulator read and write) and measured
+//    3-9% faster on every workload shape.
 //  * Operands go HBM/L2 -> LDS by direct-to-LDS DMA (global_load_lds_dwordx4),
-//    no VGPR staging, double-buffered: 2 stages x (X tile + W tile), at most
-//    128 KiB of the 160 KiB LDS.  The 64- and 128-row tiles, whose MFMA work per
-//    k-tile is too short to cover the next k-tile's loads, keep 3 or 4 stages
-//    (at most 144 KiB) and 2 or 3 k-tiles in flight (mainloop).
+//    no VGPR staging: 2 stages x (X tile + W tile), at most 128 KiB of the
+//    160 KiB LDS, 3 stages for the 224 x 192 and 192 x 192 tiles.  The 64- and
+//    128-row tiles, whose MFMA work per k-tile is too short to cover the next
+//    k-tile's loads, keep 3 or 4 stages (at most 144 KiB) and 2 or 3 k-tiles in
+//    flight.
 //  * Fragments are double-buffered in registers at k32 granularity: while
-//    the NXB x NWB MFMAs of one k32 step run, the NXB + NWB fragments of the
-//    next step are read from LDS, one read after each of the first MFMAs.  The single
-//    barrier per k-tile sits before the second k32 step: after it the next
-//    k-tile has landed and every wave has finished
-//    reading the stage that the DMA for the k-tile after next then
-//    overwrites, so the DMA runs a whole k-tile ahead and no fragment read is
-//    exposed.
+//    the MFMAs of one k32 step run, the fragments of the next step are read
+//    from LDS.  The single barrier per k-tile sits before the second k32 step:
+//    after it the next k-tile has landed and every wave has finished reading
+//    the stage that the loads of the k-tile after next then overwrite, so the
+//    loads run a whole k-tile ahead and no fragment read is exposed.
 //  * LDS tiles are 64-element (128-byte) rows; the 16-byte chunk c of row r
 //    is stored at position c ^ ((r >> 1) & 7).  A fragment read covers
 //    16 rows of one chunk column per 16 lanes; under this swizzle each group
 //    of lanes that the LDS serves together touches distinct banks.
 //  * The W fragment is the MFMA "A" operand and the X fragment the "B"
 //    operand, so each lane holds runs of four consecutive output columns of
-//    one row.  The epilogue applies bias / GELU / rounding, passes each
-//    16-row slice of a wave's tile through a private LDS area and stores
-//    whole row segments (with 256-column tiles 4 rows x 256 B fp32 or 8 rows
-//    x 128 B bf16 per instruction): direct stores from the MFMA layout cover 16 rows x 16 B
-//    per instruction and wrote 1.64x the algorithmic bytes for an fp32
+//    one row.  The epilogue applies bias / GELU / SwiGLU / rounding, passes
+//    each 16-row slice of a wave's tile through a private LDS area and stores
+//    whole row segments: direct stores from the MFMA layout cover 16 rows x
+//    16 B per instruction and wrote 1.64x the algorithmic bytes for an fp32
 //    output when measured with the 32x32 layout.  The stores are
 //    non-temporal.
 //  * Workgroups are dealt round-robin to the 8 XCDs; the tile index is
@@ -802,23 +800,23 @@ hipError_t launch_variant(const GemmParams &gp, int nxb, int nwb, hipStream_t st
 
 
 // Tile shape: the one with the least cost = (rounds of tiles over the CUs) x (tile area)
-// x (cost per flop of the shape).  The per-flop factors are measured in the bench step,
+// x (cost per flop of the shape).  The per-flop factors were measured in the bench step,
 // where the part runs at its power limit and every byte moved from L2 to LDS costs clock:
 // against 256 x 256, a 224 x 256 tile costs 2.5% more per flop, 192 x 256 5%, 256 x 192
-// 8%, 224 x 192 12% and 192 x 192 27% (rowwise 4608 x 6144 at K = 768-2304: 192 x 192 tiles
-// in three full rounds took 7% longer than 256 x 256 tiles in 1.69 rounds).  224-row tiles
-// are only considered for K >= 3072: with a short k loop the per-tile start and store
-// outweighed the finer quantization.  Ties go to the earlier (larger) shape.  Examples on
-// 256 CUs: 4608 x 2304 x 6144 takes 252 tiles of 224 x 192 (one round) instead of 216 of
-// 192 x 256 (119.8 -> 112.2 us in the bench step), 4608 x 4608 x 6144 504 of them (231.7 ->
-// 225.7 us), 4608 x 9216 x 6144 756 of 224 x 256, rowwise 4608 x 6144 x 2304 432 of 256 x 256.
+// 8%, 224 x 192 12% and 192 x 192 27%.  Ties go to the earlier (larger) shape.  Examples
+// on 256 CUs: 4608 x 2304 x 6144 takes 252 tiles of 224 x 192 (one round), 4608 x 4608 x
+// 6144 504 of them, 4608 x 9216 x 6144 756 of 224 x 256, and rowwise 4608 x 6144 x K 504 of
+// 224 x 256 at every K.  With the four-wave tiles the choice matched the fastest four-wave
+// tile on each of these shapes within 1% (a sweep of every shape, back to back); with the
+// eight-wave tiles a short k loop had favoured 256-row tiles, since a tile's start and store
+// outweighed the finer quantization.
 // 64- and 128-row tiles (plain epilogues only) serve a few hundred rows, where the larger
 // tiles leave CUs idle.  Their factors, 1.30 (128 x 256), 1.45 (128 x 192), 1.97 (64 x 256)
 // and 2.2 (64 x 192), are fitted to back-to-back runs of every tile shape on 256 to 1536 rows
 // of a 9216 x 6144 weight and three smaller products, where the choice then matched the
 // fastest shape on every one: 256 rows take 64 x 192 tiles (61.7 us against 99.6 in
 // 192 x 192), 512 rows 128 x 192 (74.0 against 104.9), 768 rows 128 x 256 (88.6 against
-// 112.3), 1024 rows 224 x 192 as before.
+// 112.3), 1024 rows 224 x 192.
 struct TileChoice {
     int nxb, nwb;
 };
