@@ -287,7 +287,9 @@ CAL_ROWS, CAL_COLS = 8192, 8192   # calibration copy: a 128 MiB bf16 weight, cop
 ATTR_LDS = "SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE"
 ATTR_WAIT = ("SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU "
              "SQ_ACTIVE_INST_LDS GRBM_GUI_ACTIVE TA_TA_BUSY TD_TD_BUSY")
-KERNEL_OF = {"gemm": "gemm_bf16_nt_kernel", "gemv": "gemv_bf16_kernel", "sum": "combine_sum_kernel",
+# "bf16_nt_kernel" matches both tiled GEMM kernels: gemm4_bf16_nt_kernel (four waves, 192- to
+# 256-row tiles: every GEMM of the step) and gemm_bf16_nt_kernel (eight waves, 64 and 128 rows).
+KERNEL_OF = {"gemm": "bf16_nt_kernel", "gemv": "gemv_bf16_kernel", "sum": "combine_sum_kernel",
              "slice": "copy_segments_kernel", "concat": "copy_segments_kernel"}
 N_XCC = 8          # GRBM_GUI_ACTIVE is counted per XCD; the CSV value is their sum
 SIMDS = 1024       # 256 CUs x 4 SIMDs
@@ -408,7 +410,7 @@ def reduce_counters(probe_json, dirs):
                       f"{(fe + wr) / e['alg']:.3f} |")
         g = fam["gemm"]
         out = {
-            "kernel": "gemm_bf16_nt_kernel", "source_sha": file_sha(GEMM_SRC),
+            "kernel": "gemm4_bf16_nt_kernel", "source_sha": file_sha(GEMM_SRC),
             "bytes_per_launch": round((g["fetch"] + g["write"]) / g["n"]),
             "algorithmic_bytes_per_launch": round(g["alg"] / g["n"]),
             "ratio_to_algorithmic": round((g["fetch"] + g["write"]) / g["alg"], 4),
@@ -1046,7 +1048,7 @@ def main():
                 "; slicing and combines on a second HIP stream, overlapping the GEMMs" if args.streams > 1 else ""),
         },
         "roofline": {
-            "kernel": "gemm_bf16_nt_kernel",
+            "kernel": "gemm4_bf16_nt_kernel",
             "bound": "mfma",
             "achieved": round(gemm_tflops, 1),
             "peak": PEAK_BF16_TFLOPS,
@@ -1527,7 +1529,7 @@ def cold_trace(trace_csv, cold_md):
 def _short_kernel(name):
     """A short label for a kernel of this library or a hipBLASLt GEMM kernel; None for others."""
     short = name.replace("void ", "").replace("tpl::(anonymous namespace)::", "").split("(")[0]
-    if short.startswith(("gemm_", "gemv_", "copy_", "combine_")):
+    if short.startswith(("gemm_", "gemm4_", "gemv_", "copy_", "combine_")):
         return short
     if "Cijk" in name:
         mt = next((t for t in name.split("_") if t.startswith("MT")), "MT?")
@@ -1604,7 +1606,7 @@ def configs_trace(path):
         name = r["Kernel_Name"]
         us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         short = name.replace("void ", "").replace("tpl::(anonymous namespace)::", "").split("(")[0]
-        if short.startswith(("gemm_", "gemv_", "copy_", "combine_")):
+        if short.startswith(("gemm_", "gemm4_", "gemv_", "copy_", "combine_")):
             g = groups.setdefault((short, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"])), ([], []))
             g[0 if "reduce" in prev else 1].append(us)
         prev = name

@@ -96,7 +96,7 @@ def test_counters_scale_bytes_by_the_calibration_copy(tmp_path, monkeypatch):
              "cal_bytes": cal}
     pj = tmp_path / "probe.json"
     pj.write_text(json.dumps(probe))
-    names = ["gemm_bf16_nt_kernel<6, true, false, 0>", "copy_segments_kernel<16>", "copy_segments_kernel<16>"]
+    names = ["gemm4_bf16_nt_kernel<7, 8, true, false, 0>", "copy_segments_kernel<16>", "copy_segments_kernel<16>"]
     runs = {"fetch": ("FETCH_SIZE", [1.0, 0.5, cal / 2048]), "write": ("WRITE_SIZE", [0.5, 1.0, cal / 1024])}
     for tag, (counter, kib) in runs.items():
         d = tmp_path / tag
@@ -136,7 +136,7 @@ def test_pmc_summary_labels_dispatches_by_their_flops(tmp_path, capsys):
     """Two runs of one program: the flops counted in the first label the same dispatch ids in
     the second, so two shapes of one kernel and grid get separate rows; hipBLASLt kernels get a
     short label and other kernels are left out."""
-    ours = "void tpl::(anonymous namespace)::gemm_bf16_nt_kernel<8, 4, true, false, 0>(tpl::GemmParams)"
+    ours = "void tpl::(anonymous namespace)::gemm4_bf16_nt_kernel<8, 8, true, false, 0>(tpl::GemmParams)"
     vend = "Cijk_Alik_Bljk_BBS_BH_Bias_HA_S_SAV_UserArgs_MT256x256x64_MI16x16x1_SK3_gfx950"
     other = "void at::native::elementwise_kernel<128, 4>(...)"
     _pmc_run(tmp_path / "a", [(1, ours, "MfmaFlopsBF16", 2e9, 1000), (1, ours, "GRBM_GUI_ACTIVE", 8 * 2000, 1000),
@@ -151,8 +151,8 @@ def test_pmc_summary_labels_dispatches_by_their_flops(tmp_path, capsys):
     rows = [dict(zip(hdr, [c.strip() for c in line.strip("|").split("|")])) for line in out[2:]]
     assert len(rows) == 3
     by = {(r["kernel"], r["GFLOP"]): r for r in rows}
-    a = by[("`gemm_bf16_nt_kernel<8, 4, true, false, 0>`", "2.0")]
-    b = by[("`gemm_bf16_nt_kernel<8, 4, true, false, 0>`", "4.0")]
+    a = by[("`gemm4_bf16_nt_kernel<8, 8, true, false, 0>`", "2.0")]
+    b = by[("`gemm4_bf16_nt_kernel<8, 8, true, false, 0>`", "4.0")]
     v = by[("`hipBLASLt MT256x256x64 stream-K`", "2.0")]
     assert a["SQ_WAIT_ANY"] == "10" and b["SQ_WAIT_ANY"] == "30" and v["SQ_WAIT_ANY"] == "5"
     # clock = GUI-active cycles per XCD over the dispatch time: 2000 cycles in 1 us = 2 GHz
