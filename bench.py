@@ -287,6 +287,10 @@ CAL_ROWS, CAL_COLS = 8192, 8192   # calibration copy: a 128 MiB bf16 weight, cop
 ATTR_LDS = "SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE"
 ATTR_WAIT = ("SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU "
              "SQ_ACTIVE_INST_LDS GRBM_GUI_ACTIVE TA_TA_BUSY TD_TD_BUSY")
+# issue back-pressure: loads refused by full TA FIFOs, LDS FIFOs full, LDS issue waits, and the
+# cycles spent sending load addresses
+ATTR_ISSUE = ("SQ_VMEM_TA_ADDR_FIFO_FULL SQ_VMEM_TA_CMD_FIFO_FULL SQ_LDS_CMD_FIFO_FULL "
+              "SQ_LDS_DATA_FIFO_FULL SQ_WAIT_INST_LDS SQ_INST_CYCLES_VMEM_RD GRBM_GUI_ACTIVE")
 # "bf16_nt_kernel" matches both tiled GEMM kernels: gemm4_bf16_nt_kernel (four waves, 192- to
 # 256-row tiles: every GEMM of the step) and gemm_bf16_nt_kernel (eight waves, 64 and 128 rows).
 KERNEL_OF = {"gemm": "bf16_nt_kernel", "gemv": "gemv_bf16_kernel", "sum": "combine_sum_kernel",
@@ -378,13 +382,14 @@ def reduce_counters(probe_json, dirs):
         e["rows"].append(i)
     md = ["# Hardware counters of one bench step, per kernel family and per GEMM shape", "",
           "Commands (run from the repository root on one MI355X; one counter set per run):", "", "```"]
-    for c in ("FETCH_SIZE", "WRITE_SIZE", "MfmaUtil MfmaFlopsBF16 GRBM_GUI_ACTIVE", ATTR_LDS, ATTR_WAIT):
+    for c in ("FETCH_SIZE", "WRITE_SIZE", "MfmaUtil MfmaFlopsBF16 GRBM_GUI_ACTIVE", ATTR_LDS, ATTR_WAIT,
+              ATTR_ISSUE):
         tag = c.split()[0].lower()
         md.append(f"rocprofv3 --pmc {c} --kernel-trace --output-format csv -d out/pmc_{tag} -o run -- "
                   f"python3 bench.py --probe out/probe_{tag}.json")
     md += ["python3 bench.py --counters out/probe_fetch_size.json out/pmc_fetch_size "
            "out/pmc_write_size out/pmc_mfmautil out/pmc_sq_lds_idx_active "
-           "out/pmc_sq_wave_cycles", "```", "",
+           "out/pmc_sq_wave_cycles out/pmc_sq_vmem_ta_addr_fifo_full", "```", "",
            f"`--probe` runs two bench steps untimed, then one copy of a {CAL_ROWS} x {CAL_COLS} bf16 weight "
            f"({probe['cal_bytes']} bytes read, the same written) whose counters calibrate the byte counts.  "
            f"The tables cover the {n} launches of the second step.  Under counter collection every dispatch "
@@ -446,14 +451,21 @@ def reduce_counters(probe_json, dirs):
     # Attribution counters, where a run collected them: per CU cycle (LDS, TA, TD activity) or
     # per wave cycle (wait and issue states; SQ_WAVE_CYCLES counts in units of 4 cycles, like
     # the wait and active counters it divides).
-    per_cu = ["SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "TA_TA_BUSY", "TD_TD_BUSY"]
+    per_cu = ["SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "TA_TA_BUSY", "TD_TD_BUSY",
+              "SQ_VMEM_TA_ADDR_FIFO_FULL", "SQ_VMEM_TA_CMD_FIFO_FULL", "SQ_LDS_CMD_FIFO_FULL",
+              "SQ_LDS_DATA_FIFO_FULL"]
     per_wave = ["SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
-                "SQ_ACTIVE_INST_LDS"]
+                "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "SQ_INST_CYCLES_VMEM_RD"]
     have = [c for c in per_cu + per_wave if any(c in p for p in per)]
     if have:
         md += ["", "## Where the GEMM's cycles go (attribution counters)", "",
                "Per CU cycle: the counter summed over the chip / (GUI-active cycles per XCD x 256 CUs).  "
-               "Per wave cycle: the counter / SQ_WAVE_CYCLES (both in units of 4 cycles).", "",
+               "Per wave cycle: the counter / SQ_WAVE_CYCLES (both in units of 4 cycles).  A ratio's "
+               "counter and divisor can come from different runs of the same step (GRBM_GUI_ACTIVE from "
+               "the last run that has it).  FIFO_FULL: cycles a load was held back by a full TA "
+               "address or command FIFO, or the LDS command or data FIFO was full; WAIT_INST_LDS: "
+               "waiting to issue an LDS instruction; INST_CYCLES_VMEM_RD: cycles sending the "
+               "addresses of loads.", "",
                "| family: shape | " + " | ".join(c.replace("SQ_", "") for c in have) + " |",
                "|---|" + "---|" * len(have)]
         for (cat, key), e in sorted(shp.items()):
