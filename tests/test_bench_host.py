@@ -121,6 +121,32 @@ def test_counters_scale_bytes_by_the_calibration_copy(tmp_path, monkeypatch):
     assert "| slice: w1 P2 | 1 | 0.0 | 0.0 | 0.0 | 1.024 |" in md
 
 
+def test_counters_normalise_issue_counters_per_cu_and_per_wave_cycle(tmp_path, monkeypatch):
+    """The issue back-pressure run: a TA FIFO-full count is divided by the CU cycles (GUI-active
+    cycles per XCD x 256 CUs: 8000 / 8 x 256), an LDS issue wait by the wave cycles."""
+    probe = {"launches": [["gemm", "colwise 8x8x8", 1024.0, 1000.0]], "cal_bytes": 1 << 27}
+    pj = tmp_path / "probe.json"
+    pj.write_text(json.dumps(probe))
+    d = tmp_path / "issue"
+    d.mkdir()
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        gemm = "gemm4_bf16_nt_kernel<7, 8, true, false, 0>"
+        for c, v in (("GRBM_GUI_ACTIVE", 8000.0), ("SQ_VMEM_TA_ADDR_FIFO_FULL", 25600.0),
+                     ("SQ_WAVE_CYCLES", 4000.0), ("SQ_WAIT_INST_LDS", 200.0)):
+            w.writerow([1, gemm, c, v])
+        w.writerow([2, "copy_segments_kernel<16>", "GRBM_GUI_ACTIVE", 10.0])
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    bench.reduce_counters(str(pj), [str(d)])
+    md = open(tmp_path / "profiles" / "dit_block_step_counters.md").read()
+    assert "| family: shape | VMEM_TA_ADDR_FIFO_FULL | WAIT_INST_LDS |" in md
+    assert "| gemm: colwise 8x8x8 | 0.100 | 0.050 |" in md
+    assert bench.ATTR_ISSUE.split()[0] == "SQ_VMEM_TA_ADDR_FIFO_FULL"   # names the run's folder
+    assert "pmc_sq_vmem_ta_addr_fifo_full" in md
+
+
 def _pmc_run(path, rows):
     """rows: (dispatch id, kernel name, counter, value, duration ns)."""
     os.makedirs(path, exist_ok=True)
